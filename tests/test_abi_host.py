@@ -1,0 +1,184 @@
+"""Host-side checks of libqgemv.so: it loads, exports exactly the C ABI that
+include/qgemv.h declares, and its argument validation rejects bad calls before
+anything reaches the GPU.  CPU only: every call here fails validation, so no
+kernel is launched and no pointer is dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import weight_only_quantized_int4_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+QG_OK, QG_ERR_NULL_POINTER, QG_ERR_BAD_SHAPE, QG_ERR_UNSUPPORTED = 0, 1, 2, 3
+QG_ERR_MISALIGNED, QG_ERR_ALIAS, QG_ERR_HIP = 4, 5, 6
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"if", "sizeof", "defined"})
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    assert names == sorted(["qgemv_int4_blockwise", "qgemv_q4k", "qgemv_q4k_dsc", "gemv_bf16",
+                            "q4k_dsc_plane_bytes", "q4k_build_dsc_plane", "qg_status_string",
+                            "qg_last_error"])
+
+
+def test_library_exports_exactly_the_header():
+    L = q.load_library()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", q.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines() if " T " in line)
+    assert exported == _declared_functions()
+
+
+def test_library_has_gfx950_code_object():
+    out = subprocess.run(["/opt/rocm/bin/roc-obj-ls", q.library_path()], capture_output=True,
+                         text=True)
+    if out.returncode != 0:
+        pytest.skip("roc-obj-ls unavailable")
+    assert "gfx950" in out.stdout
+
+
+def test_status_strings():
+    L = q.load_library()
+    names = ["QG_OK", "QG_ERR_NULL_POINTER", "QG_ERR_BAD_SHAPE", "QG_ERR_UNSUPPORTED",
+             "QG_ERR_MISALIGNED", "QG_ERR_ALIAS", "QG_ERR_HIP"]
+    for i, n in enumerate(names):
+        assert L.qg_status_string(i).decode() == n
+    assert L.qg_status_string(99).decode() == "QG_ERR_UNKNOWN"
+
+
+def test_plane_bytes():
+    assert q.q4k_dsc_plane_bytes(4096, 4096) == 4096 * 4096 // 4
+    assert q.q4k_dsc_plane_bytes(11008, 4096) == 11008 * 4096 // 4
+    assert q.q4k_dsc_plane_bytes(0, 256) == 0
+    assert q.q4k_dsc_plane_bytes(3, 100) == 0
+    assert q.q4k_dsc_plane_bytes(-1, 256) == 0
+
+
+# Fake, never-dereferenced device addresses (16-byte aligned, far apart).
+A = 0x7F0000000000
+B = 0x7F0100000000
+C = 0x7F0200000000
+D = 0x7F0300000000
+E = 0x7F0400000000
+
+
+def _int4(L, x=A, ldx=64, w=B, s=C, zp=D, y=E, ldy=16, yt=0, M=1, N=16, K=64, bs=32):
+    return L.qgemv_int4_blockwise(x, ldx, w, s, zp, y, ldy, yt, M, N, K, bs, None)
+
+
+def test_int4_validation():
+    L = q.load_library()
+    assert _int4(L, x=None) == QG_ERR_NULL_POINTER
+    assert _int4(L, s=None) == QG_ERR_NULL_POINTER
+    assert _int4(L, y=None) == QG_ERR_NULL_POINTER
+    for M in (0, 9, -1):
+        assert _int4(L, M=M) == QG_ERR_BAD_SHAPE
+        assert f"M = {M}" in L.qg_last_error().decode()
+    assert _int4(L, N=-1) == QG_ERR_BAD_SHAPE
+    assert _int4(L, K=0) == QG_ERR_BAD_SHAPE
+    assert _int4(L, K=96, bs=64) == QG_ERR_BAD_SHAPE       # K % bs != 0
+    assert _int4(L, bs=16) == QG_ERR_UNSUPPORTED
+    assert _int4(L, bs=48) == QG_ERR_UNSUPPORTED
+    assert _int4(L, yt=7) == QG_ERR_UNSUPPORTED
+    assert _int4(L, ldx=32) == QG_ERR_BAD_SHAPE
+    assert _int4(L, ldy=8) == QG_ERR_BAD_SHAPE
+    assert _int4(L, w=B + 8) == QG_ERR_MISALIGNED
+    assert _int4(L, x=A + 1) == QG_ERR_MISALIGNED
+    assert _int4(L, y=E + 2, yt=2) == QG_ERR_MISALIGNED
+    assert _int4(L, y=B + 16) == QG_ERR_ALIAS               # y inside w
+    assert _int4(L, y=A + 64) == QG_ERR_ALIAS               # y inside x (x spans 128 B)
+    assert _int4(L, zp=E + 8) == QG_ERR_ALIAS               # zero points overlap y
+    # N == 0 is an empty problem: OK, nothing enqueued (no GPU needed)
+    assert _int4(L, N=0) == QG_OK
+    assert L.qg_last_error().decode() == ""
+    # a huge w is refused up front (kernels address with 32-bit offsets)
+    assert _int4(L, N=1 << 20, K=1 << 13, ldx=1 << 13, ldy=1 << 20) == QG_ERR_UNSUPPORTED
+
+
+def _q4k(L, x=A, ldx=256, w=B, y=E, ldy=16, M=1, N=16, K=256, dsc=None, use_dsc=False):
+    if use_dsc:
+        return L.qgemv_q4k_dsc(x, ldx, w, dsc, y, ldy, M, N, K, None)
+    return L.qgemv_q4k(x, ldx, w, y, ldy, M, N, K, None)
+
+
+def test_q4k_validation():
+    L = q.load_library()
+    assert _q4k(L, w=None) == QG_ERR_NULL_POINTER
+    assert _q4k(L, K=300, ldx=300) == QG_ERR_BAD_SHAPE
+    assert _q4k(L, K=128, ldx=128) == QG_ERR_BAD_SHAPE
+    assert _q4k(L, M=9) == QG_ERR_BAD_SHAPE
+    assert _q4k(L, w=B + 4) == QG_ERR_MISALIGNED
+    assert _q4k(L, x=A + 2) == QG_ERR_MISALIGNED
+    assert _q4k(L, y=B + 64) == QG_ERR_ALIAS
+    assert _q4k(L, N=0) == QG_OK
+    # the plane entry point never falls back silently
+    assert _q4k(L, use_dsc=True, dsc=None) == QG_ERR_NULL_POINTER
+    assert "NULL" in L.qg_last_error().decode()
+    assert _q4k(L, use_dsc=True, dsc=C + 8) == QG_ERR_MISALIGNED
+    assert _q4k(L, use_dsc=True, dsc=E) == QG_ERR_ALIAS
+
+
+def test_plane_builder_validation():
+    L = q.load_library()
+    assert L.q4k_build_dsc_plane(None, C, 4, 256, None) == QG_ERR_NULL_POINTER
+    assert L.q4k_build_dsc_plane(B, C, 4, 100, None) == QG_ERR_BAD_SHAPE
+    assert L.q4k_build_dsc_plane(B, C, -1, 256, None) == QG_ERR_BAD_SHAPE
+    assert L.q4k_build_dsc_plane(B + 1, C, 4, 256, None) == QG_ERR_MISALIGNED
+    assert L.q4k_build_dsc_plane(B, B + 32, 4, 256, None) == QG_ERR_ALIAS
+    assert L.q4k_build_dsc_plane(B, C, 0, 256, None) == QG_OK
+
+
+def _bf16(L, x=A, ldx=64, w=B, ldw=64, y=E, ldy=16, yt=1, M=1, N=16, K=64):
+    return L.gemv_bf16(x, ldx, w, ldw, y, ldy, yt, M, N, K, None)
+
+
+def test_bf16_validation():
+    L = q.load_library()
+    assert _bf16(L, w=None) == QG_ERR_NULL_POINTER
+    assert _bf16(L, M=9) == QG_ERR_BAD_SHAPE
+    assert _bf16(L, K=0) == QG_ERR_BAD_SHAPE
+    assert _bf16(L, ldw=63) == QG_ERR_BAD_SHAPE
+    assert _bf16(L, x=A + 1) == QG_ERR_MISALIGNED
+    assert _bf16(L, w=B + 1) == QG_ERR_MISALIGNED
+    assert _bf16(L, y=B + 2) == QG_ERR_ALIAS
+    assert _bf16(L, yt=5) == QG_ERR_UNSUPPORTED
+    assert _bf16(L, N=0) == QG_OK
+
+
+def test_binding_raises_with_library_message():
+    x = torch.zeros(9, 64, dtype=torch.float16)
+    w = torch.zeros(4, 32, dtype=torch.uint8)
+    s = torch.zeros(4, 2, dtype=torch.float16)
+    y = torch.zeros(9, 4, dtype=torch.float16)
+    with pytest.raises(q.QgemvError) as ei:
+        q.qgemv_int4_blockwise(x, w, s, None, y, 32, stream=0)
+    assert ei.value.status == QG_ERR_BAD_SHAPE
+    assert "M = 9" in str(ei.value)
+    with pytest.raises(q.QgemvError) as ei:
+        q.qgemv_q4k_dsc(torch.zeros(1, 256), torch.zeros(4, 144, dtype=torch.uint8), None,
+                        torch.zeros(1, 4), stream=0)
+    assert ei.value.status == QG_ERR_NULL_POINTER
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "weight_only_quantized_int4_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

@@ -1,0 +1,113 @@
+"""GPU parity of gemv_bf16 (MI355X).
+
+Workloads: (1536 x 1536), (256 x 1536), (1536 x 6912), (6912 x 1536) at
+M = 1..8; the unaligned-tail path with K in {7, 12, 100, 1534} at N in
+{256, 1536}; 2-byte base offsets on x and W; every output type; the current
+stream; invariants.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_quantized_int4_amd as q
+from gpu_cases import DEV, OUT_NAME, assert_accept, bf16_case, bf16_dev, say, y_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _ref(p, M, cols=None, ldw=None, wbuf=None, xbuf=None, ldx=None):
+    xb = p.x[:M] if xbuf is None else xbuf
+    wb = p.w if wbuf is None else wbuf
+    return oracle.bf16_gemv(np.ascontiguousarray(xb), np.ascontiguousarray(wb), M, p.N, p.K,
+                            p.K if ldx is None else ldx, p.K if ldw is None else ldw, cols=cols)
+
+
+@pytest.mark.parametrize("N,K,seed", [(1536, 1536, 301), (256, 1536, 302), (1536, 6912, 303),
+                                      (6912, 1536, 304)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+def test_decode_shapes(N, K, seed, M):
+    p = bf16_case(N, K, seed)
+    say(f"bf16 N={N} K={K} M={M}")
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    q.gemv_bf16(bf16_dev(p.x[:M]), bf16_dev(p.w), y)
+    yr, S = _ref(p, M)
+    assert_accept(y_host(y), yr, S, "bf16", f"bf16 {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("N", [256, 1536])
+@pytest.mark.parametrize("K", [7, 12, 100, 1534])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_unaligned_k(N, K, M):
+    p = bf16_case(N, K, 310 + K + N)
+    say(f"bf16 unaligned K={K} N={N} M={M}")
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_bf16(bf16_dev(p.x[:M]), bf16_dev(p.w), y)
+    yr, S = _ref(p, M)
+    assert_accept(y_host(y), yr, S, "f32", f"bf16 unaligned K={K}")
+
+
+@pytest.mark.parametrize("K", [12, 1534, 4096])
+@pytest.mark.parametrize("off", [1, 3, 7])
+def test_storage_offsets(K, off):
+    N, M = 300, 4
+    p = bf16_case(N, K, 320 + K)
+    # W and x both start `off` elements into their buffers
+    wbuf = np.zeros(off + N * K, dtype=np.uint16)
+    wbuf[off:] = p.w.ravel()
+    xbuf = np.zeros(off + M * K, dtype=np.uint16)
+    xbuf[off:] = p.x[:M].ravel()
+    wd = bf16_dev(wbuf)[off:].view(N, K)
+    xd = bf16_dev(xbuf)[off:].view(M, K)
+    say(f"bf16 offset={off} K={K}")
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_bf16(xd, wd, y)
+    yr, S = _ref(p, M)
+    assert_accept(y_host(y), yr, S, "f32", f"bf16 offset {off}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32, torch.float16])
+def test_output_types(out_dtype):
+    p = bf16_case(512, 2048, 330)
+    say(f"bf16 out={out_dtype}")
+    y = torch.full((2, 512), float("nan"), dtype=out_dtype, device=DEV)
+    q.gemv_bf16(bf16_dev(p.x[:2]), bf16_dev(p.w), y)
+    yr, S = _ref(p, 2)
+    assert_accept(y_host(y), yr, S, OUT_NAME[out_dtype], "bf16 out types")
+
+
+def test_long_unaligned_k_multi_chunk():
+    # M = 8 stages 2040 elements per pass in the general path: K = 6911 -> 4 passes
+    N, K, M = 200, 6911, 8
+    p = bf16_case(N, K, 340)
+    say("bf16 general path multi-chunk")
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_bf16(bf16_dev(p.x[:M]), bf16_dev(p.w), y)
+    yr, S = _ref(p, M)
+    assert_accept(y_host(y), yr, S, "f32", "bf16 general multi-chunk")
+
+
+def test_invariants_and_stream():
+    p = bf16_case(1536, 1536, 301)
+    xd, wd = bf16_dev(p.x[:4]), bf16_dev(p.w)
+    say("bf16 invariants")
+    y = torch.empty((4, 1536), dtype=torch.float32, device=DEV)
+    q.gemv_bf16(xd, wd, y)
+    base = y_host(y)
+    q.gemv_bf16(xd, wd, y)
+    assert np.array_equal(base, y_host(y))
+    q.gemv_bf16(-xd, wd, y)
+    assert np.array_equal(y_host(y), -base)
+    # the call is enqueued on the caller's current stream
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    y2 = torch.zeros((4, 1536), dtype=torch.float32, device=DEV)
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(50_000_000)
+        q.gemv_bf16(xd, wd, y2)
+        ev = torch.cuda.Event()
+        ev.record(s)
+    assert not ev.query()
+    assert torch.cuda.default_stream().query()
+    s.synchronize()
+    assert np.array_equal(y_host(y2), base)

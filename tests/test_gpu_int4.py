@@ -1,0 +1,222 @@
+"""GPU parity of qgemv_int4_blockwise against the fp64 oracle (MI355X).
+
+Workloads: the int4 decode shapes -- (256 x 1536, block 32, asymmetric, M=1),
+(1536 x 1536) and (1536 x 6912) with block 128 and the implicit zero point 8,
+M = 1..8, and the lm_head shape (151936 x 4096, block 32, asymmetric) at M = 1
+and 8 on sampled columns -- plus block sizes 64/256, every output type, ragged
+N, strided and unaligned x, multi-chunk K, a one-hot dequant probe (bit-exact),
+and invariants.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import weight_only_quantized_int4_amd as q
+from gpu_cases import (DEV, OUT_NAME, assert_accept, f16_dev, int4_case, int4_ref, say,
+                       to_dev, y_host)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(p, M, out_dtype=torch.float16, x=None, ldy=None):
+    xd = f16_dev(p.x[:M]) if x is None else x
+    wd = to_dev(p.w)
+    sd = f16_dev(p.scales)
+    zd = None if p.zp is None else to_dev(p.zp)
+    if ldy is None:
+        y = torch.full((M, p.N), float("nan"), dtype=out_dtype, device=DEV)
+    else:
+        y = torch.full((M, ldy), float("nan"), dtype=out_dtype, device=DEV)[:, :p.N]
+    q.qgemv_int4_blockwise(xd, wd, sd, zd, y, p.block_size)
+    return y
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_small_decode_shape_block32_asym(M):
+    # 256 x 1536, block 32, asymmetric zero points, fp16 out
+    say(f"int4 N=256 K=1536 bs=32 asym M={M}")
+    p = int4_case(256, 1536, 32, True, 101)
+    y = y_host(_run(p, M))
+    yr, S = int4_ref(256, 1536, 32, True, 101)
+    assert_accept(y, yr[:M], S[:M], "f16", f"int4 256x1536 M={M}")
+
+
+@pytest.mark.parametrize("K,seed", [(1536, 201), (6912, 202)])
+@pytest.mark.parametrize("M", list(range(1, 9)))
+def test_symmetric_block128_sweep(K, seed, M):
+    say(f"int4 N=1536 K={K} bs=128 sym M={M}")
+    p = int4_case(1536, K, 128, False, seed)
+    y = y_host(_run(p, M))
+    yr, S = int4_ref(1536, K, 128, False, seed)
+    assert_accept(y, yr[:M], S[:M], "f16", f"int4 1536x{K} M={M}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("bs", [32, 64, 128, 256])
+def test_block_sizes_and_output_types(bs, out_dtype):
+    N, K = 1000, 2048  # ragged N (not a multiple of any row tile)
+    say(f"int4 N={N} K={K} bs={bs} asym M=3 out={out_dtype}")
+    p = int4_case(N, K, bs, True, 7 + bs)
+    y = y_host(_run(p, 3, out_dtype))
+    yr, S = int4_ref(N, K, bs, True, 7 + bs)
+    assert_accept(y, yr[:3], S[:3], OUT_NAME[out_dtype], f"int4 bs={bs}")
+
+
+def test_odd_block_count_and_tiny_shapes():
+    for (N, K, bs) in [(1, 32, 32), (3, 96, 32), (17, 160, 32), (5, 384, 128)]:
+        say(f"int4 tiny N={N} K={K} bs={bs}")
+        p = int4_case(N, K, bs, True, N * K)
+        for M in (1, 8):
+            y = y_host(_run(p, M, torch.float32))
+            yr, S = int4_ref(N, K, bs, True, N * K)
+            assert_accept(y, yr[:M], S[:M], "f32", f"int4 tiny {N}x{K} M={M}")
+
+
+def test_strided_and_unaligned_x_and_strided_y():
+    N, K, bs, M = 300, 1024, 32, 5
+    say("int4 strided/unaligned x, strided y")
+    p = int4_case(N, K, bs, True, 55)
+    yr, S = int4_ref(N, K, bs, True, 55)
+    # x rows with ldx = K + 3 and a 2-byte base offset
+    buf = np.zeros(1 + M * (K + 3), dtype=np.uint16)
+    for m in range(M):
+        buf[1 + m * (K + 3):1 + m * (K + 3) + K] = p.x[m]
+    xt = f16_dev(buf)[1:].view(M, K + 3)[:, :K]
+    assert xt.data_ptr() % 16 == 2
+    y = y_host(_run(p, M, torch.float16, x=xt, ldy=N + 5))
+    assert_accept(y, yr[:M], S[:M], "f16", "int4 strided")
+
+
+def test_multi_chunk_k():
+    # M = 8 puts at most 3264 elements of x in LDS per pass: K = 8192 takes 3 passes
+    N, K = 512, 8192
+    say(f"int4 multi-chunk N={N} K={K} M=8")
+    p = int4_case(N, K, 32, True, 77)
+    y = y_host(_run(p, 8, torch.float32))
+    yr, S = int4_ref(N, K, 32, True, 77)
+    assert_accept(y, yr, S, "f32", "int4 multi-chunk")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_lm_head_shape_sampled(M):
+    N, K = 151936, 4096
+    say(f"int4 lm_head N={N} K={K} bs=32 asym M={M}")
+    p = int4_case(N, K, 32, True, 501)
+    y = y_host(_run(p, M))
+    rng = np.random.default_rng(1)
+    cols = tuple(sorted(set(rng.integers(0, N, 600).tolist()) | {0, 1, N - 2, N - 1}))
+    yr, S = int4_ref(N, K, 32, True, 501, cols)
+    assert_accept(y[:, list(cols)], yr[:M], S[:M], "f16", f"int4 lm_head M={M}")
+    assert np.all(np.isfinite(y))
+
+
+def test_one_hot_probe_is_bit_exact():
+    """x = e_k, fp32 out: y[n] must equal the oracle's dequantized w[n,k] bitwise."""
+    N, K, bs = 64, 512, 32
+    p = int4_case(N, K, bs, True, 31)
+    wdq = oracle.int4_dequant(p.w, p.scales, p.zp, N, K, bs)
+    wd, sd, zd = to_dev(p.w), f16_dev(p.scales), to_dev(p.zp)
+    ks = list(range(0, 64)) + list(range(64, K, 7)) + [K - 1]
+    say(f"int4 one-hot probe {len(ks)} columns of x")
+    xs = torch.zeros((len(ks), K), dtype=torch.float16, device=DEV)
+    for i, k in enumerate(ks):
+        xs[i, k] = 1.0
+    ys = torch.empty((len(ks), N), dtype=torch.float32, device=DEV)
+    for i in range(len(ks)):
+        q.qgemv_int4_blockwise(xs[i:i + 1], wd, sd, zd, ys[i:i + 1], bs)
+    got = ys.cpu().numpy()
+    want = wdq[:, ks].T.astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_lm_head_one_hot_sampled():
+    N, K, bs = 151936, 4096, 32
+    p = int4_case(N, K, bs, True, 501)
+    wd, sd, zd = to_dev(p.w), f16_dev(p.scales), to_dev(p.zp)
+    rng = np.random.default_rng(2)
+    rows = sorted(set(rng.integers(0, N, 300).tolist()) | {N - 1})
+    for k in [0, 31, 32, 2047, 4095]:
+        say(f"int4 lm_head one-hot k={k}")
+        x = torch.zeros((1, K), dtype=torch.float16, device=DEV)
+        x[0, k] = 1.0
+        y = torch.empty((1, N), dtype=torch.float32, device=DEV)
+        q.qgemv_int4_blockwise(x, wd, sd, zd, y, bs)
+        got = y.cpu().numpy()[0, rows]
+        want = oracle.int4_dequant(p.w, p.scales, p.zp, N, K, bs, rows=rows)[:, k].astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), k
+
+
+def test_invariants():
+    N, K, bs, M = 512, 1024, 32, 8
+    say("int4 invariants")
+    p = int4_case(N, K, bs, True, 91)
+    base = y_host(_run(p, M, torch.float32))
+    # determinism
+    again = y_host(_run(p, M, torch.float32))
+    assert np.array_equal(base, again)
+    # y(-x) == -y(x) and y(4x) == 4 y(x), bitwise
+    neg = p.x[:M] ^ np.uint16(0x8000)
+    yn = y_host(_run(p, M, torch.float32, x=f16_dev(neg)))
+    assert np.array_equal(yn, -base)
+    x4 = (f16_dev(p.x[:M]).float() * 4).half()
+    y4 = y_host(_run(p, M, torch.float32, x=x4))
+    assert np.array_equal(y4, 4 * base)
+    # every code equal to its zero point -> y == 0 exactly
+    zp_nib = np.empty((N, K // bs), dtype=np.uint8)
+    zp_nib[:, 0::2] = p.zp & 15
+    zp_nib[:, 1::2] = p.zp >> 4
+    per_k = np.repeat(zp_nib, bs, axis=1)
+    wz = (per_k[:, 0::2] | (per_k[:, 1::2] << 4)).astype(np.uint8)
+    y0 = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.qgemv_int4_blockwise(f16_dev(p.x[:M]), to_dev(wz), f16_dev(p.scales), to_dev(p.zp), y0, bs)
+    assert np.all(y_host(y0) == 0.0)
+    # column permutation of (w, scales, zp) permutes y bitwise
+    perm = np.random.default_rng(5).permutation(N)
+    yp = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    q.qgemv_int4_blockwise(f16_dev(p.x[:M]), to_dev(p.w[perm]), f16_dev(p.scales[perm]),
+                           to_dev(p.zp[perm]), yp, bs)
+    assert np.array_equal(y_host(yp), base[:, perm])
+    # row m of an M = 8 call equals the M = 1 call on that row (x fits LDS in one pass)
+    for m in (0, 5):
+        y1 = torch.empty((1, N), dtype=torch.float32, device=DEV)
+        q.qgemv_int4_blockwise(f16_dev(p.x[m:m + 1]), to_dev(p.w), f16_dev(p.scales),
+                               to_dev(p.zp), y1, bs)
+        assert np.array_equal(y_host(y1)[0], base[m])
+
+
+def test_empty_and_rejected_calls_on_device():
+    p = int4_case(16, 64, 32, True, 3)
+    say("int4 N=0 and M=9 on device")
+    xd, wd, sd, zd = f16_dev(p.x[:1]), to_dev(p.w), f16_dev(p.scales), to_dev(p.zp)
+    y = torch.full((1, 16), 7.0, dtype=torch.float16, device=DEV)
+    L = q.load_library()
+    st = torch.cuda.current_stream().cuda_stream
+    assert L.qgemv_int4_blockwise(xd.data_ptr(), 64, wd.data_ptr(), sd.data_ptr(), zd.data_ptr(),
+                                  y.data_ptr(), 16, 0, 1, 0, 64, 32, st) == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    with pytest.raises(q.QgemvError):
+        x9 = torch.zeros((9, 64), dtype=torch.float16, device=DEV)
+        y9 = torch.zeros((9, 16), dtype=torch.float16, device=DEV)
+        q.qgemv_int4_blockwise(x9, wd, sd, zd, y9, 32)
+
+
+def test_uses_current_stream():
+    p = int4_case(256, 1536, 32, True, 101)
+    xd, wd, sd, zd = f16_dev(p.x[:1]), to_dev(p.w), f16_dev(p.scales), to_dev(p.zp)
+    y = torch.zeros((1, 256), dtype=torch.float16, device=DEV)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say("int4 current-stream")
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(50_000_000)
+        q.qgemv_int4_blockwise(xd, wd, sd, zd, y, 32)
+        ev = torch.cuda.Event()
+        ev.record(s)
+    assert not ev.query(), "work did not go to the caller's stream"
+    assert torch.cuda.default_stream().query()
+    s.synchronize()
+    yr, S = int4_ref(256, 1536, 32, True, 101)
+    assert_accept(y_host(y), yr[:1], S[:1], "f16", "int4 stream")

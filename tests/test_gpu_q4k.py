@@ -1,0 +1,150 @@
+"""GPU parity of qgemv_q4k, q4k_build_dsc_plane and qgemv_q4k_dsc (MI355X).
+
+Workloads: the 7B-decoder q4_K layer shapes (4096 x 4096), (11008 x 4096),
+(4096 x 11008) at M = 1, direct decode and through the W_dsc plane; M = 1..8
+on smaller shapes; the plane byte-exact against the oracle's plane over a
+matrix of shapes (the page's host-mirror-vs-device test); direct and plane
+paths bitwise equal; a one-hot dequant probe (bit-exact); invariants.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_quantized_int4_amd as q
+from gpu_cases import DEV, assert_accept, q4k_case, q4k_ref, say, to_dev, y_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _plane(wd, N, K):
+    dsc = torch.empty((q.q4k_dsc_plane_bytes(N, K) // 8, 2), dtype=torch.float32, device=DEV)
+    q.q4k_build_dsc_plane(wd, dsc, N, K)
+    return dsc
+
+
+@pytest.mark.parametrize("N,K,seed", [(4096, 4096, 401), (11008, 4096, 402), (4096, 11008, 403)])
+def test_decoder_layer_shapes_direct_and_plane(N, K, seed):
+    p = q4k_case(N, K, seed)
+    xd, wd = to_dev(p.x[:1]), to_dev(p.w)
+    yr, S = q4k_ref(N, K, seed, 1)
+    say(f"q4k direct N={N} K={K}")
+    y1 = torch.full((1, N), float("nan"), device=DEV)
+    q.qgemv_q4k(xd, wd, y1)
+    yd = y_host(y1)
+    assert_accept(yd, yr, S, "f32", f"q4k direct {N}x{K}")
+    say(f"q4k plane build + dsc N={N} K={K}")
+    dsc = _plane(wd, N, K)
+    y2 = torch.full((1, N), float("nan"), device=DEV)
+    q.qgemv_q4k_dsc(xd, wd, dsc, y2)
+    yp = y_host(y2)
+    assert_accept(yp, yr, S, "f32", f"q4k dsc {N}x{K}")
+    # one kernel, one summation order: the two paths agree bitwise
+    assert np.array_equal(yd.view(np.uint64), yp.view(np.uint64))
+
+
+@pytest.mark.parametrize("N,K", [(2, 256), (6, 512), (4096, 256), (2, 4096), (6, 11008),
+                                 (4096, 4096), (11008, 4096), (4096, 11008), (37, 768)])
+def test_plane_byte_exact(N, K):
+    p = q4k_case(N, K, 1000 + N + K)
+    say(f"q4k plane byte-exact N={N} K={K}")
+    got = _plane(to_dev(p.w), N, K).cpu().numpy()
+    want = oracle.q4k_build_plane(p.w, N, K)
+    assert got.tobytes() == want.tobytes()
+
+
+def test_plane_signed_zero_mins():
+    """m == 0 must give -0.0 (bits 0x80000000) in the plane."""
+    N, K = 64, 512
+    p = q4k_case(N, K, 5)
+    w = p.w.reshape(N, 2, 144).copy()
+    w[:, :, 8:12] = 0        # mins of chunks 0..3 and top bits of chunks 4..7
+    w[:, :, 12:16] &= 0x0F   # low bits of the mins of chunks 4..7
+    w = w.reshape(N, 288)
+    say("q4k plane signed zero")
+    got = _plane(to_dev(w), N, K).cpu().numpy()
+    assert np.all(got[:, 1].view(np.uint32) == 0x80000000)
+    assert got.tobytes() == oracle.q4k_build_plane(w, N, K).tobytes()
+
+
+@pytest.mark.parametrize("M", list(range(1, 9)))
+def test_m_sweep(M):
+    N, K = 1000, 4096
+    p = q4k_case(N, K, 420)
+    yr, S = q4k_ref(N, K, 420)
+    xd, wd = to_dev(p.x[:M]), to_dev(p.w)
+    say(f"q4k M={M} N={N} K={K}")
+    y = torch.full((M, N), float("nan"), device=DEV)
+    q.qgemv_q4k(xd, wd, y)
+    yd = y_host(y)
+    assert_accept(yd, yr[:M], S[:M], "f32", f"q4k M={M}")
+    y2 = torch.full((M, N), float("nan"), device=DEV)
+    q.qgemv_q4k_dsc(xd, wd, _plane(wd, N, K), y2)
+    assert np.array_equal(yd, y_host(y2))
+
+
+def test_multi_chunk_k_and_strided_x():
+    # M = 8 stages at most 1792 elements of x per pass: K = 11008 takes 7 passes
+    N, K, M = 300, 11008, 8
+    p = q4k_case(N, K, 421)
+    yr, S = q4k_ref(N, K, 421)
+    buf = np.zeros((M, K + 3), dtype=np.float32)
+    buf[:, 1:K + 1] = p.x[:M]
+    xt = to_dev(buf)[:, 1:K + 1]  # ldx = K + 3, 4-byte (not 16-byte) aligned
+    say("q4k multi-chunk strided x")
+    y = torch.full((M, N + 2), float("nan"), device=DEV)[:, :N]
+    q.qgemv_q4k(xt, to_dev(p.w), y)
+    assert_accept(y_host(y), yr, S, "f32", "q4k multi-chunk")
+
+
+def test_one_hot_probe_is_bit_exact():
+    N, K = 96, 512
+    p = q4k_case(N, K, 77)
+    wdq = oracle.q4k_dequant(p.w, N, K).astype(np.float32)
+    wd = to_dev(p.w)
+    dsc = _plane(wd, N, K)
+    ks = list(range(0, 256, 3)) + list(range(256, K, 5)) + [K - 1]
+    say(f"q4k one-hot probe {len(ks)} columns")
+    for use_plane in (False, True):
+        got = np.empty((len(ks), N), dtype=np.float32)
+        for i, k in enumerate(ks):
+            x = torch.zeros((1, K), device=DEV)
+            x[0, k] = 1.0
+            y = torch.empty((1, N), device=DEV)
+            if use_plane:
+                q.qgemv_q4k_dsc(x, wd, dsc, y)
+            else:
+                q.qgemv_q4k(x, wd, y)
+            got[i] = y.cpu().numpy()[0]
+        assert np.array_equal(got.view(np.uint32), wdq[:, ks].T.copy().view(np.uint32)), use_plane
+
+
+def test_invariants():
+    N, K, M = 512, 1024, 8
+    p = q4k_case(N, K, 99)
+    xd, wd = to_dev(p.x[:M]), to_dev(p.w)
+    say("q4k invariants")
+    y = torch.empty((M, N), device=DEV)
+    q.qgemv_q4k(xd, wd, y)
+    base = y_host(y)
+    q.qgemv_q4k(xd, wd, y)
+    assert np.array_equal(base, y_host(y))
+    q.qgemv_q4k(-xd, wd, y)
+    assert np.array_equal(y_host(y), -base)
+    q.qgemv_q4k(xd * 0.25, wd, y)
+    assert np.array_equal(y_host(y), 0.25 * base)
+    # all quants 0 and all mins 0 -> y == 0
+    w0 = p.w.reshape(N, 4, 144).copy()
+    w0[:, :, 16:] = 0
+    w0[:, :, 8:12] = 0
+    w0[:, :, 12:16] &= 0x0F
+    q.qgemv_q4k(xd, to_dev(w0.reshape(N, 576)), y)
+    assert np.all(y_host(y) == 0.0)
+
+
+def test_null_plane_is_rejected_on_device():
+    p = q4k_case(16, 256, 1)
+    say("q4k null plane")
+    with pytest.raises(q.QgemvError) as ei:
+        q.qgemv_q4k_dsc(to_dev(p.x[:1]), to_dev(p.w), None, torch.empty((1, 16), device=DEV))
+    assert ei.value.status_name == "QG_ERR_NULL_POINTER"

@@ -1,0 +1,11 @@
+"""MI355X-native weight-only quantized decode GEMV (int4 MatMulNBits, q4_K, bf16).
+
+The compute lives in ``libqgemv.so`` (hand-written HIP kernels for gfx950 behind
+a C ABI, see ``include/qgemv.h``).  ``qgemv`` is the thin ctypes binding with
+the same entry-point names; PyTorch only supplies device memory and streams.
+"""
+from .qgemv import (  # noqa: F401
+    QG_BF16, QG_F16, QG_F32, QgemvError, gemv_bf16, library_path, load_library,
+    q4k_build_dsc_plane, q4k_dsc_plane_bytes, qgemv_int4_blockwise, qgemv_q4k,
+    qgemv_q4k_dsc,
+)

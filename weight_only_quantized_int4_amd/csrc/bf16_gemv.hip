@@ -1,0 +1,219 @@
+// bf16_gemv.hip -- dense bf16 GEMV for gfx950, M = 1..8, any K >= 1 and any
+// 2-byte storage offset of x and W.
+//
+// Operation (the bf16 GEMV primitive of the AstrAI backend commit list):
+//     y[m,n] = sum_k x[m,k] * w[n,k]
+//
+// Two kernels, chosen per call on the host:
+//  * aligned: x and W rows 16-byte aligned and K a multiple of 8 (the
+//    production case with allocator-aligned tensors).  Pure 128-bit weight
+//    loads, x staged as bf16 in LDS, v_dot2_f32_bf16 (exact bf16 products,
+//    fp32 accumulation) -- no branch inside the loop.
+//  * general: any alignment.  Each row's 128-bit loads are anchored at the
+//    row's first 16-byte-aligned element h (0..7); the h head elements and
+//    the < 8 tail elements are swept one at a time.  x is staged in LDS as
+//    fp32 (so it can be read at any element offset) in K-chunks with an
+//    8-element halo, and every product is one fp32 FMA.
+// Both keep one row per group of LPR lanes and reduce with cross-lane
+// shuffles; no split-K (measured as a regression on the page).
+#include "qgemv_device.h"
+#include "qgemv_launch.h"
+
+namespace qg {
+namespace {
+
+template <int M, int LPR, int R>
+__global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw,
+    void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int KC) {
+  extern __shared__ uint4 xs[];  // [M][KC/8] bf16
+  constexpr int S = kBlock / LPR;
+  const int tid = threadIdx.x;
+  const int slot = tid / LPR;
+  const int j = tid % LPR;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int G = KC >> 3;
+
+  // Rows past the end load the last row (results never stored): no branches.
+  int rows[R];
+  uint32_t wo[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    rows[i] = (tile * R + i) * S + slot;
+    wo[i] = (uint32_t)(rows[i] < N ? rows[i] : N - 1) * (uint32_t)ldw;
+  }
+  float acc[R][M];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
+
+  for (int kc = 0; kc < K; kc += KC) {
+    const int kn = min(KC, K - kc);
+    const int P = kn >> 3;
+    auto load = [&](uint4 (&v)[R], int p) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) v[i] = load_stream16(w + (wo[i] + (uint32_t)(kc + 8 * p)));
+    };
+    uint4 cur[R];
+    if (j < P) load(cur, j);
+    __syncthreads();
+    for (int t = tid; t < M * P; t += kBlock) {
+      const int m = t / P, i = t - m * P;
+      xs[m * G + i] = *reinterpret_cast<const uint4*>(x + m * ldx + kc + 8 * i);
+    }
+    __syncthreads();
+    for (int p = j; p < P; p += LPR) {
+      uint4 nxt[R];
+      const bool more = p + LPR < P;
+      if (more) load(nxt, p + LPR);
+      const uint4* wv = cur;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint4 xv = xs[m * G + p];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          float t = acc[i][m];
+          t = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(wv[i].x), bitcast<bf16x2>(xv.x), t, false);
+          t = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(wv[i].y), bitcast<bf16x2>(xv.y), t, false);
+          t = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(wv[i].z), bitcast<bf16x2>(xv.z), t, false);
+          t = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(wv[i].w), bitcast<bf16x2>(xv.w), t, false);
+          acc[i][m] = t;
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) cur[i] = nxt[i];
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float v = group_sum<LPR>(acc[i][m]);
+      if (j == 0 && rows[i] < N) store_out(y, m * ldy + rows[i], v, y_type);
+    }
+}
+
+template <int M, int LPR>
+__global__ __launch_bounds__(kBlock) void bf16_gemv_general(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw,
+    void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int KC) {
+  extern __shared__ float xf[];  // [M][KC + 8] fp32, chunk plus halo
+  const int XS = KC + 8;
+  constexpr int S = kBlock / LPR;
+  const int tid = threadIdx.x;
+  const int slot = tid / LPR;
+  const int j = tid % LPR;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int n = tile * S + slot;
+  const bool live = n < N;
+  const uint16_t* wr = w + (int64_t)(live ? n : 0) * ldw;
+  // Anchor: first element of the row whose address is 16-byte aligned.
+  int h = (int)(((16u - (uint32_t)(reinterpret_cast<uintptr_t>(wr) & 15u)) & 15u) >> 1);
+  if (h > K) h = K;
+  const int nbody = (K - h) >> 3;
+  const int t0 = h + (nbody << 3);
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+
+  for (int kc = 0; kc < K; kc += KC) {
+    const int kn = min(KC, K - kc);
+    const int ext = min(kn + 8, K - kc);
+    __syncthreads();
+    for (int t = tid; t < M * ext; t += kBlock) {
+      const int m = t / ext, e = t - m * ext;
+      xf[m * XS + e] = __uint_as_float((uint32_t)x[m * ldx + kc + e] << 16);
+    }
+    __syncthreads();
+    if (!live) continue;
+
+    // head: k in [0, h)
+    for (int k = kc + j; k < min(h, kc + kn); k += LPR) {
+      const float wf = __uint_as_float((uint32_t)wr[k] << 16);
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(wf, xf[m * XS + (k - kc)], acc[m]);
+    }
+    // body: 16-byte pieces starting at h + 8i that begin inside this chunk
+    const int i_lo = (kc > h) ? (kc - h + 7) >> 3 : 0;
+    const int e_hi = kc + kn - h;
+    const int i_hi = min(nbody, e_hi > 0 ? (e_hi + 7) >> 3 : 0);
+    for (int i = i_lo + j; i < i_hi; i += LPR) {
+      const int s0 = h + 8 * i;
+      const uint4 v = load_stream16(wr + s0);
+      const float wv[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                           bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float* xp = xf + m * XS + (s0 - kc);
+        float a = acc[m];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = __builtin_fmaf(wv[e], xp[e], a);
+        acc[m] = a;
+      }
+    }
+    // tail: k in [t0, K)
+    for (int k = max(kc, t0) + j; k < kc + kn; k += LPR) {
+      const float wf = __uint_as_float((uint32_t)wr[k] << 16);
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(wf, xf[m * XS + (k - kc)], acc[m]);
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const float v = group_sum<LPR>(acc[m]);
+    if (j == 0 && live) store_out(y, m * ldy + n, v, y_type);
+  }
+}
+
+template <int M>
+hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
+                    int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
+  const bool aligned = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0) &&
+                       ((reinterpret_cast<uintptr_t>(w) & 15) == 0) && (ldw % 8 == 0) &&
+                       (K % 8 == 0);
+  if (aligned) {
+    constexpr int LPR = 16;
+    constexpr int R = (M <= 4) ? 2 : 1;
+    constexpr int RT = (kBlock / LPR) * R;
+    const int grid = (N + RT - 1) / RT;
+    int KC = (kLdsBudget / (2 * M)) & ~7;
+    if (KC > K) KC = K;
+    const size_t shmem = (size_t)M * KC * 2;
+    hipLaunchKernelGGL((bf16_gemv_aligned<M, LPR, R>), dim3(grid), dim3(kBlock), shmem, stream,
+                       x, ldx, w, ldw, y, ldy, y_type, N, K, KC);
+  } else {
+    constexpr int LPR = 16;
+    constexpr int S = kBlock / LPR;
+    const int grid = (N + S - 1) / S;
+    int KC = (kLdsBudget / (4 * M) - 8) & ~7;
+    if (KC > K) KC = K;
+    const size_t shmem = (size_t)M * (KC + 8) * 4;
+    hipLaunchKernelGGL((bf16_gemv_general<M, LPR>), dim3(grid), dim3(kBlock), shmem, stream, x,
+                       ldx, w, ldw, y, ldy, y_type, N, K, KC);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bf16_gemv(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,
+                            void* y, int64_t ldy, int y_type, int M, int N, int K,
+                            hipStream_t stream) {
+  switch (M) {
+#define QG_CASE(MM) \
+  case MM:          \
+    return launch_m<MM>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+    QG_CASE(1) QG_CASE(2) QG_CASE(3) QG_CASE(4) QG_CASE(5) QG_CASE(6) QG_CASE(7) QG_CASE(8)
+#undef QG_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qg

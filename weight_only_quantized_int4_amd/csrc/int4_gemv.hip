@@ -1,0 +1,264 @@
+// int4_gemv.hip -- MatMulNBits-style blockwise int4 GEMV for gfx950, M = 1..8.
+//
+// Operation (onnx-genai pull request #1000, "Summary" and "What it does": the
+// M = 1 int4 MatMulNBits decode GEMV with per-column fp32 accumulation):
+//     y[m,n] = sum_k x[m,k] * s[n,k/bs] * (q[n,k] - zp[n,k/bs])
+//
+// Design (MI355X-first; the page's multicol NC=4 CUDA kernel is prior art only):
+//  * The weight matrix is one contiguous byte stream ([N][K/2]).  A
+//    workgroup (256 threads = 4 wavefronts) owns a tile of rows; inside it a
+//    group of LPR consecutive lanes owns one row and walks that row's 16-byte
+//    pieces (32 nibbles = 32 weights) with a stride of LPR pieces, so every
+//    wavefront load instruction reads 64/LPR contiguous runs of LPR*16 bytes.
+//    Each lane owns R rows at once so that every x value read from LDS is
+//    used R times.
+//  * x is staged once per workgroup in LDS, pre-permuted within every group of
+//    8 elements to (x0,x4 | x1,x5 | x2,x6 | x3,x7) so that it lines up with the
+//    nibble pairs below.  Each 64-byte piece of x is followed by 16 bytes of
+//    padding: the lanes of a row read pieces 80 bytes apart, which spreads
+//    their 16-byte LDS reads over distinct banks.
+//  * Unpack: OR-ing a nibble into the mantissa of fp16 1024.0 gives 1024+q
+//    exactly; a nibble sitting 4 bits higher gives 1024+16q.  One packed fp16
+//    add (or fma by 1/16) with -(1024+zp) (or -(64+zp)) then yields q-zp
+//    exactly as a pair of fp16 values: 9 VALU ops per 8 weights.  The zero
+//    point is subtracted per weight, so all-zero-point weights give y = 0
+//    exactly.
+//  * MAC: v_dot2_f32_f16 multiplies an exact (q-zp) pair by an x pair and
+//    accumulates in fp32 (the products are exact).  The per-block fp16 scale
+//    (exact in fp32) is applied once per 32-weight piece with one fp32 FMA, so
+//    dequantized weights never leave registers and a one-hot x reproduces
+//    s*(q-zp) bit-exactly.
+//  * Reduction: the LPR lanes of a row reduce with cross-lane shuffles; no
+//    atomics and no cross-workgroup split-K (the AstrAI commit list measured
+//    split-K as a regression).
+#include "qgemv_device.h"
+#include "qgemv_launch.h"
+
+namespace qg {
+namespace {
+
+struct Pairs8 {
+  f16x2 a, b, c, d;  // (e0,e4)-zp, (e1,e5)-zp, (e2,e6)-zp, (e3,e7)-zp
+};
+
+// Eight 4-bit codes of one 32-bit word (element 2i in the low nibble of byte
+// i) -> four exact fp16 pairs of (code - zero point).  `magic` is fp16 1024.0
+// in both halves, held in a VGPR so that each mask-and-or is one v_and_or_b32.
+__device__ __forceinline__ Pairs8 unpack8(uint32_t word, uint32_t magic, uint32_t bias_lo,
+                                          uint32_t bias_hi) {
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t w8 = word >> 8;
+  Pairs8 r;
+  r.a = bitcast<f16x2>((word & 0x000F000Fu) | magic) + bitcast<f16x2>(bias_lo);
+  r.b = __builtin_elementwise_fma(bitcast<f16x2>((word & 0x00F000F0u) | magic), sixteenth,
+                                  bitcast<f16x2>(bias_hi));
+  r.c = bitcast<f16x2>((w8 & 0x000F000Fu) | magic) + bitcast<f16x2>(bias_lo);
+  r.d = __builtin_elementwise_fma(bitcast<f16x2>((w8 & 0x00F000F0u) | magic), sixteenth,
+                                  bitcast<f16x2>(bias_hi));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Everything one lane loads for one 16-byte piece of R rows.
+template <int R>
+struct Piece {
+  uint4 w[R];
+  uint32_t s[R];  // fp16 scale bits
+  uint32_t z[R];  // zero-point byte (both nibbles)
+};
+
+template <int M, int LPR, int R, bool ZP>
+__global__ __launch_bounds__(kBlock) void int4_gemv_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zp, int zrow,
+    void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int bs_log2, int KC,
+    int x_vec16) {
+  extern __shared__ uint4 xs[];  // [M][KC/32][5]: 4 permuted groups of 8 halves + pad
+  constexpr int S = kBlock / LPR;  // row slots per workgroup
+  const int tid = threadIdx.x;
+  const int slot = tid / LPR;
+  const int j = tid % LPR;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int nb = K >> bs_log2;
+  const int PS = (KC >> 5) * 5;  // uint4 slots per x row in LDS
+  const uint32_t magic = vreg_const(0x64006400u);
+
+  // Rows past the end are clamped to the last row for loading (no branches in
+  // the stream); their results are never stored.  Offsets are 32-bit (the
+  // host rejects tensors of 4 GiB or more), so every load is a uniform base
+  // address plus one VGPR offset.
+  int rows[R];
+  uint32_t wo[R], so[R], zo[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    rows[i] = (tile * R + i) * S + slot;
+    const uint32_t nl = (uint32_t)(rows[i] < N ? rows[i] : N - 1);
+    wo[i] = nl * (uint32_t)(K >> 1);
+    so[i] = nl * (uint32_t)nb;
+    zo[i] = nl * (uint32_t)zrow;
+  }
+
+  auto load = [&](Piece<R>& st, int gp) {
+    const uint32_t blk = (uint32_t)((gp << 5) >> bs_log2);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      st.w[i] = load_stream16(w + (wo[i] + (uint32_t)gp * 16u));
+      st.s[i] = scales[so[i] + blk];
+      st.z[i] = ZP ? zp[zo[i] + (blk >> 1)] : 0x88u;
+    }
+  };
+
+  float acc[R][M];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
+
+  for (int kc = 0; kc < K; kc += KC) {
+    const int kn = min(KC, K - kc);
+    const int P = kn >> 5;
+    const int gp0 = kc >> 5;
+    // Issue the first piece's loads before staging x: their latency overlaps
+    // the staging and the barrier.
+    Piece<R> cur;
+    if (j < P) load(cur, gp0 + j);
+
+    __syncthreads();
+    const int groups = kn >> 3;
+    for (int t = tid; t < M * groups; t += kBlock) {
+      const int m = t / groups;
+      const int gi = t - m * groups;
+      const uint16_t* src = x + m * ldx + kc + gi * 8;
+      uint32_t h[8];
+      if (x_vec16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        h[0] = v.x & 0xFFFFu; h[1] = v.x >> 16; h[2] = v.y & 0xFFFFu; h[3] = v.y >> 16;
+        h[4] = v.z & 0xFFFFu; h[5] = v.z >> 16; h[6] = v.w & 0xFFFFu; h[7] = v.w >> 16;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = src[e];
+      }
+      xs[m * PS + (gi >> 2) * 5 + (gi & 3)] = make_uint4(
+          h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16), h[3] | (h[7] << 16));
+    }
+    __syncthreads();
+
+    for (int p = j; p < P; p += LPR) {
+      // Prefetch the next piece while this one is computed.
+      Piece<R> nxt;
+      const bool more = p + LPR < P;
+      if (more) load(nxt, gp0 + p + LPR);
+
+      const int gp = gp0 + p;
+      const int zsh = (((gp << 5) >> bs_log2) & 1) << 2;
+      float sc[R];
+      uint32_t blo[R], bhi[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        sc[i] = f16_to_f32(cur.s[i]);
+        const uint32_t z = (cur.z[i] >> zsh) & 15u;
+        blo[i] = (0xE400u + z) * 0x00010001u;         // -(1024 + zp) in both halves
+        bhi[i] = (0xD400u + (z << 4)) * 0x00010001u;  // -(64 + zp) in both halves
+      }
+      float part[R][M];
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m) part[i][m] = 0.f;
+
+      const uint4* xp = xs + p * 5;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint4 xv[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xv[m] = xp[m * PS + d];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const Pairs8 q = unpack8(word_of(cur.w[i], d), magic, blo[i], bhi[i]);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float t = part[i][m];
+            t = __builtin_amdgcn_fdot2(q.a, bitcast<f16x2>(xv[m].x), t, false);
+            t = __builtin_amdgcn_fdot2(q.b, bitcast<f16x2>(xv[m].y), t, false);
+            t = __builtin_amdgcn_fdot2(q.c, bitcast<f16x2>(xv[m].z), t, false);
+            t = __builtin_amdgcn_fdot2(q.d, bitcast<f16x2>(xv[m].w), t, false);
+            part[i][m] = t;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[i][m] = __builtin_fmaf(sc[i], part[i][m], acc[i][m]);
+      if (more) cur = nxt;
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float v = group_sum<LPR>(acc[i][m]);
+      if (j == 0 && rows[i] < N) store_out(y, m * ldy + rows[i], v, y_type);
+    }
+}
+
+template <int M, int LPR, int R>
+hipError_t launch_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* scales,
+                      const uint8_t* zp, void* y, int64_t ldy, int y_type, int N, int K,
+                      int block_size, hipStream_t stream) {
+  constexpr int RT = (kBlock / LPR) * R;
+  const int grid = (N + RT - 1) / RT;
+  // x takes 80 bytes of LDS per 32 elements and row.
+  int KC = (kLdsBudget / (80 * M)) * 32;
+  if (KC > K) KC = K;
+  const int bs_log2 = __builtin_ctz((unsigned)block_size);
+  const int zrow = ((K / block_size) + 1) / 2;
+  const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
+  const size_t shmem = (size_t)M * (KC / 32) * 80;
+  if (zp)
+    hipLaunchKernelGGL((int4_gemv_kernel<M, LPR, R, true>), dim3(grid), dim3(kBlock), shmem,
+                       stream, x, ldx, w, scales, zp, zrow, y, ldy, y_type, N, K, bs_log2, KC,
+                       x_vec16);
+  else
+    hipLaunchKernelGGL((int4_gemv_kernel<M, LPR, R, false>), dim3(grid), dim3(kBlock), shmem,
+                       stream, x, ldx, w, scales, zp, zrow, y, ldy, y_type, N, K, bs_log2, KC,
+                       x_vec16);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* scales,
+                    const uint8_t* zp, void* y, int64_t ldy, int y_type, int N, int K,
+                    int block_size, hipStream_t stream) {
+  const int P = K / 32;  // 16-byte pieces per row
+  // Lanes per row: a divisor of the piece count when possible so that no
+  // lane idles in the last stride of a row.
+  const bool lpr8 = (P % 16 != 0) && (P % 8 == 0);
+  constexpr int R = 2;
+  if (lpr8)
+    return launch_cfg<M, 8, R>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+  return launch_cfg<M, 16, R>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+}
+
+}  // namespace
+
+hipError_t launch_int4_gemv(const uint16_t* x, int64_t ldx, const uint8_t* w,
+                            const uint16_t* scales, const uint8_t* zp, void* y, int64_t ldy,
+                            int y_type, int M, int N, int K, int block_size,
+                            hipStream_t stream) {
+  switch (M) {
+#define QG_CASE(MM) \
+  case MM:          \
+    return launch_m<MM>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+    QG_CASE(1) QG_CASE(2) QG_CASE(3) QG_CASE(4) QG_CASE(5) QG_CASE(6) QG_CASE(7) QG_CASE(8)
+#undef QG_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qg

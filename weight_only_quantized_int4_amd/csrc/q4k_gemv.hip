@@ -1,0 +1,309 @@
+// q4k_gemv.hip -- q4_K GEMV for gfx950 (coefficients decoded in the kernel or
+// read from a W_dsc plane), and the load-time W_dsc plane builder.
+//
+// Operation ("62 . r59 -- q4_K W_dsc plane + riders", sections 2.1-2.3 and 3.2):
+// a q4_K row is K/256 super-blocks of 144 bytes (fp16 d, fp16 dmin, twelve
+// bytes of packed 6-bit scales/mins, 128 bytes of 4-bit quants).  Chunk c of
+// 32 weights has the rank-1 coefficients dv = d*sc(c), mv = -(dmin*m(c)), and
+// its weights are w = dv*q + mv.  The W_dsc plane stores (dv, mv) chunk-major:
+// entry (c, n) at float2 index c*N + n.
+//
+// Design:
+//  * One kernel template serves both entry points: DSC=false decodes (dv, mv)
+//    from the super-block header, DSC=true loads them from the plane.  Every
+//    other instruction, and so the summation order, is shared, which makes
+//    the two results bitwise equal whenever the plane matches the weights
+//    (the same structural argument the page makes for its two kernel
+//    instances).
+//  * A "piece" is 32 quant bytes of one super-block = chunks 2g and 2g+1
+//    (64 weights).  A group of LPR lanes (LPR a multiple of 4) owns a row; lane
+//    j always has the same g = j % 4, so its half-pair of the 6-bit decode is
+//    loop-invariant and branch-free.
+//  * Rank-1 factorisation per chunk: sum_l (dv*q_l + mv) x_l is evaluated as
+//    dv * (sum_l q_l x_l) + mv * (sum_l x_l).  The chunk sums of x are computed
+//    once per workgroup while x is staged in LDS, so the inner loop spends one
+//    fp32 FMA per weight (v_fma_mix_f32 on an exact fp16 quant).  With a one-hot
+//    x this still reproduces w = RN(dv*q + mv) bit-exactly.
+//  * Quants are converted with the fp16 1024.0 mantissa trick (exact), as in
+//    the int4 kernel.
+//  * x lives in LDS as fp32 with 4 floats of padding after every 64: the
+//    lanes of a row read pieces 272 bytes apart, so their 16-byte LDS reads
+//    fall in distinct banks (without the padding all of them would hit the
+//    same bank).
+#include "qgemv_device.h"
+#include "qgemv_launch.h"
+
+namespace qg {
+namespace {
+
+constexpr int kQ4kBlockBytes = 144;
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// (sc, m) of chunks 2g and 2g+1 from the twelve packed bytes (words A = bytes
+// 0..3, B = 4..7, C = 8..11), as two bytes each: s2 = sc(2g) | sc(2g+1) << 8.
+// get_scale_min_k4, branch-free over the lane's g:
+//   chunk < 4 : sc = A.byte[c] & 63,  m = B.byte[c] & 63
+//   chunk >= 4: sc = (C.byte[c-4] & 15) | ((A.byte[c-4] >> 6) << 4)
+//               m  = (C.byte[c-4] >> 4) | ((B.byte[c-4] >> 6) << 4)
+// For both halves the two bytes sit at byte offset 2*(g&1) of their words.
+__device__ __forceinline__ void scale_min_pair(uint32_t A, uint32_t B, uint32_t C, int g,
+                                               uint32_t& s2, uint32_t& m2) {
+  const int sh = (g & 1) << 4;
+  const uint32_t a = A >> sh, b = B >> sh, c = C >> sh;
+  if (g < 2) {
+    s2 = a & 0x3F3Fu;
+    m2 = b & 0x3F3Fu;
+  } else {
+    s2 = (c & 0x0F0Fu) | ((a >> 2) & 0x3030u);
+    m2 = ((c >> 4) & 0x0F0Fu) | ((b >> 2) & 0x3030u);
+  }
+}
+
+// What one lane loads for one piece: 32 quant bytes and either the 16-byte
+// header (decoded in the kernel) or the two plane entries.
+struct Q4kPiece {
+  uint4 q0, q1;
+  uint4 h;      // header (DSC = false)
+  float2 ea, eb;  // plane entries of chunks 2g and 2g+1 (DSC = true)
+};
+
+template <int M, int LPR, bool DSC>
+__global__ __launch_bounds__(kBlock) void q4k_gemv_kernel(
+    const float* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
+    const float2* __restrict__ dsc, float* __restrict__ y, int64_t ldy, int N, int K, int KC,
+    int x_vec16) {
+  static_assert(LPR % 4 == 0, "a lane's pair index g must be fixed");
+  extern __shared__ float smem[];
+  const int XSTR = (KC >> 6) * 68;  // floats per x row in LDS (64 + 4 pad per piece)
+  float* xs = smem;                 // [M][KC/64][68]
+  float* sx = smem + M * XSTR;      // [M][KC/32] chunk sums of x
+  const int KC32 = KC >> 5;
+  constexpr int S = kBlock / LPR;
+  const int tid = threadIdx.x;
+  const int slot = tid / LPR;
+  const int j = tid % LPR;
+  const int g = j & 3;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int n = tile * S + slot;
+  // Rows past the end load the last row (results never stored): no branches.
+  const uint32_t nl = (uint32_t)(n < N ? n : N - 1);
+  const int nsb = K >> 8;
+  const uint32_t wo = nl * (uint32_t)nsb * (uint32_t)kQ4kBlockBytes;
+
+  const uint32_t magic = vreg_const(0x64006400u);
+  const f16x2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const f16x2 m64 = {(_Float16)-64.0f, (_Float16)-64.0f};
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+
+  auto load = [&](Q4kPiece& st, int sb) {
+    const uint32_t bo = wo + (uint32_t)sb * kQ4kBlockBytes;
+    st.q0 = load_stream16(w + (bo + 16u + 32u * g));
+    st.q1 = load_stream16(w + (bo + 32u + 32u * g));
+    if constexpr (DSC) {
+      const uint32_t c = (uint32_t)sb * 8u + 2u * g;
+      st.ea = load_stream8f(dsc + (c * (uint32_t)N + nl));
+      st.eb = load_stream8f(dsc + ((c + 1u) * (uint32_t)N + nl));
+    } else {
+      st.h = load_stream16(w + bo);
+    }
+  };
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+
+  for (int kc = 0; kc < K; kc += KC) {
+    const int kn = min(KC, K - kc);
+    const int P = kn >> 6;  // (super-block, g) pieces in this chunk
+    const int sb0 = kc >> 8;
+    // First piece's loads go out before x is staged.
+    Q4kPiece cur;
+    if (j < P) load(cur, sb0 + (j >> 2));
+
+    __syncthreads();
+    if (x_vec16) {
+      const int v4 = kn >> 2;
+      for (int t = tid; t < M * v4; t += kBlock) {
+        const int m = t / v4, i = t - m * v4;
+        const int e = 4 * i;
+        *reinterpret_cast<float4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) =
+            *reinterpret_cast<const float4*>(x + m * ldx + kc + e);
+      }
+    } else {
+      for (int t = tid; t < M * kn; t += kBlock) {
+        const int m = t / kn, i = t - m * kn;
+        xs[m * XSTR + (i >> 6) * 68 + (i & 63)] = x[m * ldx + kc + i];
+      }
+    }
+    __syncthreads();
+    const int nch = kn >> 5;
+    for (int t = tid; t < M * nch; t += kBlock) {
+      const int m = t / nch, c = t - m * nch;
+      const float* src = xs + m * XSTR + (c >> 1) * 68 + 32 * (c & 1);
+      float s = 0.f;
+#pragma unroll
+      for (int l = 0; l < 32; ++l) s += src[l];
+      sx[m * KC32 + c] = s;
+    }
+    __syncthreads();
+
+    for (int p = j; p < P; p += LPR) {
+      Q4kPiece nxt;
+      const bool more = p + LPR < P;
+      if (more) load(nxt, sb0 + ((p + LPR) >> 2));
+
+      float dva, mva, dvb, mvb;
+      if constexpr (DSC) {
+        dva = cur.ea.x; mva = cur.ea.y; dvb = cur.eb.x; mvb = cur.eb.y;
+      } else {
+        uint32_t s2, m2;
+        scale_min_pair(cur.h.y, cur.h.z, cur.h.w, g, s2, m2);
+        const float d = f16_to_f32(cur.h.x & 0xFFFFu);
+        const float dmin = f16_to_f32(cur.h.x >> 16);
+        dva = d * (float)(s2 & 0xFFu);
+        dvb = d * (float)(s2 >> 8);
+        mva = -(dmin * (float)(m2 & 0xFFu));
+        mvb = -(dmin * (float)(m2 >> 8));
+      }
+
+      float pa[M], pb[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) pa[m] = pb[m] = 0.f;
+      const float* xa = xs + p * 68;  // chunk 2g; chunk 2g+1 at +32
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t word = t < 4 ? word_of(cur.q0, t) : word_of(cur.q1, t - 4);
+        const uint32_t w8 = word >> 8;
+        // chunk 2g: low nibbles of bytes (0,2) and (1,3); chunk 2g+1: high nibbles
+        const f16x2 A = bitcast<f16x2>((word & 0x000F000Fu) | magic) + m1024;
+        const f16x2 C = bitcast<f16x2>((w8 & 0x000F000Fu) | magic) + m1024;
+        const f16x2 B =
+            __builtin_elementwise_fma(bitcast<f16x2>((word & 0x00F000F0u) | magic), sixteenth, m64);
+        const f16x2 D =
+            __builtin_elementwise_fma(bitcast<f16x2>((w8 & 0x00F000F0u) | magic), sixteenth, m64);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const float4 xa4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 4 * t);
+          const float4 xb4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 32 + 4 * t);
+          float u = pa[m], v = pb[m];
+          u = __builtin_fmaf((float)A.x, xa4.x, u);
+          u = __builtin_fmaf((float)C.x, xa4.y, u);
+          u = __builtin_fmaf((float)A.y, xa4.z, u);
+          u = __builtin_fmaf((float)C.y, xa4.w, u);
+          v = __builtin_fmaf((float)B.x, xb4.x, v);
+          v = __builtin_fmaf((float)D.x, xb4.y, v);
+          v = __builtin_fmaf((float)B.y, xb4.z, v);
+          v = __builtin_fmaf((float)D.y, xb4.w, v);
+          pa[m] = u;
+          pb[m] = v;
+        }
+      }
+      const int ca = 2 * p;  // chunk index within this K-chunk (= 8*(p/4) + 2g)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float a = acc[m];
+        a = __builtin_fmaf(dva, pa[m], a);
+        a = __builtin_fmaf(mva, sx[m * KC32 + ca], a);
+        a = __builtin_fmaf(dvb, pb[m], a);
+        a = __builtin_fmaf(mvb, sx[m * KC32 + ca + 1], a);
+        acc[m] = a;
+      }
+      if (more) cur = nxt;
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const float v = group_sum<LPR>(acc[m]);
+    if (j == 0 && n < N) y[m * ldy + n] = v;
+  }
+}
+
+// One thread per (super-block sb, row n), n fastest: decode the header once,
+// write the eight (dv, mv) pairs of the super-block.  For a fixed chunk the
+// writes of consecutive threads are consecutive float2s.
+__global__ __launch_bounds__(kBlock) void q4k_plane_kernel(const uint8_t* __restrict__ w,
+                                                           float2* __restrict__ dsc, int N,
+                                                           int nsb) {
+  const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (t >= (int64_t)N * nsb) return;
+  const int n = (int)(t % N);
+  const int sb = (int)(t / N);
+  const uint4 h = *reinterpret_cast<const uint4*>(w + ((int64_t)n * nsb + sb) * kQ4kBlockBytes);
+  const float d = f16_to_f32(h.x & 0xFFFFu);
+  const float dmin = f16_to_f32(h.x >> 16);
+  uint32_t sc[12];
+  const uint32_t words[3] = {h.y, h.z, h.w};
+#pragma unroll
+  for (int i = 0; i < 12; ++i) sc[i] = (words[i >> 2] >> ((i & 3) * 8)) & 0xFFu;
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) {
+    uint32_t s, m;
+    if (cc < 4) {
+      s = sc[cc] & 63u;
+      m = sc[cc + 4] & 63u;
+    } else {
+      s = (sc[cc + 4] & 15u) | ((sc[cc - 4] >> 6) << 4);
+      m = (sc[cc + 4] >> 4) | ((sc[cc] >> 6) << 4);
+    }
+    const float dv = d * (float)s;        // one binary32 multiply (exact)
+    const float mv = -(dmin * (float)m);  // exact negation: -0.0 when the product is 0
+    dsc[((int64_t)sb * 8 + cc) * N + n] = make_float2(dv, mv);
+  }
+}
+
+template <int M, int LPR>
+hipError_t launch_cfg(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
+                      int64_t ldy, int N, int K, hipStream_t stream) {
+  constexpr int S = kBlock / LPR;
+  const int grid = (N + S - 1) / S;
+  // x (68 floats per 64 elements) plus its chunk sums (2 floats per 64), fp32,
+  // within the LDS budget; KC a multiple of 256 (whole super-blocks).
+  int KC = (kLdsBudget / (4 * 70 * M)) * 64 & ~255;
+  if (KC > K) KC = K;
+  const size_t shmem = (size_t)M * ((KC / 64) * 68 + KC / 32) * 4;
+  const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 4 == 0);
+  if (dsc)
+    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, true>), dim3(grid), dim3(kBlock), shmem, stream,
+                       x, ldx, w, reinterpret_cast<const float2*>(dsc), y, ldy, N, K, KC,
+                       x_vec16);
+  else
+    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, false>), dim3(grid), dim3(kBlock), shmem, stream,
+                       x, ldx, w, nullptr, y, ldy, N, K, KC, x_vec16);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_m(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
+                    int64_t ldy, int N, int K, hipStream_t stream) {
+  return launch_cfg<M, 16>(x, ldx, w, dsc, y, ldy, N, K, stream);
+}
+
+}  // namespace
+
+hipError_t launch_q4k_gemv(const float* x, int64_t ldx, const uint8_t* w, const float* dsc,
+                           float* y, int64_t ldy, int M, int N, int K, hipStream_t stream) {
+  switch (M) {
+#define QG_CASE(MM) \
+  case MM:          \
+    return launch_m<MM>(x, ldx, w, dsc, y, ldy, N, K, stream);
+    QG_CASE(1) QG_CASE(2) QG_CASE(3) QG_CASE(4) QG_CASE(5) QG_CASE(6) QG_CASE(7) QG_CASE(8)
+#undef QG_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_q4k_build_plane(const uint8_t* w, float* dsc, int N, int K, hipStream_t stream) {
+  const int nsb = K / 256;
+  const int64_t total = (int64_t)N * nsb;
+  const int grid = (int)((total + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL(q4k_plane_kernel, dim3(grid), dim3(kBlock), 0, stream, w,
+                     reinterpret_cast<float2*>(dsc), N, nsb);
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -1,0 +1,224 @@
+// qgemv_api.cpp -- the C ABI of libqgemv.so (declared in include/qgemv.h).
+//
+// Every entry point validates its arguments on the host -- pointers, shapes,
+// strides, alignment, dtype, aliasing -- and only then enqueues exactly one
+// kernel on the caller's stream.  Nothing is allocated and nothing is
+// synchronised.  A failed validation enqueues nothing and records a
+// human-readable detail for qg_last_error() in thread-local storage.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "qgemv.h"
+#include "qgemv_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512];
+
+qg_status ok() {
+  g_last_error[0] = '\0';
+  return QG_OK;
+}
+
+__attribute__((format(printf, 2, 3))) qg_status fail(qg_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+qg_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(QG_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// Kernels address every tensor with 32-bit byte offsets.
+constexpr int64_t kMaxTensorBytes = int64_t(1) << 32;
+
+int dtype_size(int32_t t) { return t == QG_F32 ? 4 : 2; }
+
+bool valid_out_dtype(int32_t t) { return t == QG_F16 || t == QG_BF16 || t == QG_F32; }
+
+// Common shape checks.  Returns QG_OK or the failure already recorded.
+qg_status check_mnk(const char* fn, int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > 8) return fail(QG_ERR_BAD_SHAPE, "%s: M = %lld, must be in 1..8", fn, (long long)M);
+  if (N < 0) return fail(QG_ERR_BAD_SHAPE, "%s: N = %lld < 0", fn, (long long)N);
+  if (K < 1) return fail(QG_ERR_BAD_SHAPE, "%s: K = %lld < 1", fn, (long long)K);
+  if (N > INT32_MAX || K > INT32_MAX)
+    return fail(QG_ERR_BAD_SHAPE, "%s: N or K exceeds 2^31-1", fn);
+  return QG_OK;
+}
+
+qg_status check_ld(const char* fn, const char* name, int64_t ld, int64_t need) {
+  if (ld < need)
+    return fail(QG_ERR_BAD_SHAPE, "%s: %s = %lld < %lld", fn, name, (long long)ld, (long long)need);
+  return QG_OK;
+}
+
+}  // namespace
+
+// The library is built with hidden visibility; only the C ABI is exported.
+#pragma GCC visibility push(default)
+extern "C" {
+
+const char* qg_status_string(qg_status s) {
+  switch (s) {
+    case QG_OK: return "QG_OK";
+    case QG_ERR_NULL_POINTER: return "QG_ERR_NULL_POINTER";
+    case QG_ERR_BAD_SHAPE: return "QG_ERR_BAD_SHAPE";
+    case QG_ERR_UNSUPPORTED: return "QG_ERR_UNSUPPORTED";
+    case QG_ERR_MISALIGNED: return "QG_ERR_MISALIGNED";
+    case QG_ERR_ALIAS: return "QG_ERR_ALIAS";
+    case QG_ERR_HIP: return "QG_ERR_HIP";
+  }
+  return "QG_ERR_UNKNOWN";
+}
+
+const char* qg_last_error(void) { return g_last_error; }
+
+qg_status qgemv_int4_blockwise(const uint16_t* x, int64_t ldx, const uint8_t* w,
+                               const uint16_t* scales, const uint8_t* zero_points, void* y,
+                               int64_t ldy, int32_t y_type, int64_t M, int64_t N, int64_t K,
+                               int32_t block_size, void* stream) {
+  static const char fn[] = "qgemv_int4_blockwise";
+  if (!x || !w || !scales || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w, scales and y are required", fn);
+  if (qg_status s = check_mnk(fn, M, N, K)) return s;
+  if (block_size != 32 && block_size != 64 && block_size != 128 && block_size != 256)
+    return fail(QG_ERR_UNSUPPORTED, "%s: block_size %d not in {32, 64, 128, 256}", fn, block_size);
+  if (K % block_size != 0)
+    return fail(QG_ERR_BAD_SHAPE, "%s: K = %lld is not a multiple of block_size %d", fn,
+                (long long)K, block_size);
+  if (!valid_out_dtype(y_type)) return fail(QG_ERR_UNSUPPORTED, "%s: y_type %d", fn, y_type);
+  if (qg_status s = check_ld(fn, "ldx", ldx, K)) return s;
+  if (qg_status s = check_ld(fn, "ldy", ldy, N)) return s;
+  if (!aligned(w, 16)) return fail(QG_ERR_MISALIGNED, "%s: w must be 16-byte aligned", fn);
+  if (!aligned(x, 2) || !aligned(scales, 2))
+    return fail(QG_ERR_MISALIGNED, "%s: x and scales must be 2-byte aligned", fn);
+  const int ysz = dtype_size(y_type);
+  if (!aligned(y, ysz)) return fail(QG_ERR_MISALIGNED, "%s: y must be %d-byte aligned", fn, ysz);
+  const int64_t nb = K / block_size;
+  const int64_t zrow = (nb + 1) / 2;
+  if (N * (K / 2) >= kMaxTensorBytes)
+    return fail(QG_ERR_UNSUPPORTED, "%s: w is 4 GiB or larger (kernels use 32-bit offsets)", fn);
+  const Range ry = range_of(y, ((M - 1) * ldy + N) * ysz);
+  if (N > 0 && (overlap(ry, range_of(x, ((M - 1) * ldx + K) * 2)) ||
+                overlap(ry, range_of(w, N * (K / 2))) || overlap(ry, range_of(scales, N * nb * 2)) ||
+                (zero_points && overlap(ry, range_of(zero_points, N * zrow)))))
+    return fail(QG_ERR_ALIAS, "%s: y overlaps an input", fn);
+  if (N == 0) return ok();
+  return hip_status(qg::launch_int4_gemv(x, ldx, w, scales, zero_points, y, ldy, y_type, (int)M,
+                                         (int)N, (int)K, block_size,
+                                         static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+static qg_status q4k_common(const char* fn, const float* x, int64_t ldx, const uint8_t* w,
+                            const float* dsc, float* y, int64_t ldy, int64_t M, int64_t N,
+                            int64_t K, void* stream) {
+  if (qg_status s = check_mnk(fn, M, N, K)) return s;
+  if (K % 256 != 0)
+    return fail(QG_ERR_BAD_SHAPE, "%s: K = %lld is not a multiple of 256", fn, (long long)K);
+  if (N * (K / 256) * 144 >= kMaxTensorBytes)
+    return fail(QG_ERR_UNSUPPORTED, "%s: w is 4 GiB or larger (kernels use 32-bit offsets)", fn);
+  if (qg_status s = check_ld(fn, "ldx", ldx, K)) return s;
+  if (qg_status s = check_ld(fn, "ldy", ldy, N)) return s;
+  if (!aligned(w, 16)) return fail(QG_ERR_MISALIGNED, "%s: w must be 16-byte aligned", fn);
+  if (dsc && !aligned(dsc, 16)) return fail(QG_ERR_MISALIGNED, "%s: dsc must be 16-byte aligned", fn);
+  if (!aligned(x, 4) || !aligned(y, 4))
+    return fail(QG_ERR_MISALIGNED, "%s: x and y must be 4-byte aligned", fn);
+  const Range ry = range_of(y, ((M - 1) * ldy + N) * 4);
+  if (N > 0 && (overlap(ry, range_of(x, ((M - 1) * ldx + K) * 4)) ||
+                overlap(ry, range_of(w, N * (K / 256) * 144)) ||
+                (dsc && overlap(ry, range_of(dsc, N * K / 4)))))
+    return fail(QG_ERR_ALIAS, "%s: y overlaps an input", fn);
+  if (N == 0) return ok();
+  return hip_status(qg::launch_q4k_gemv(x, ldx, w, dsc, y, ldy, (int)M, (int)N, (int)K,
+                                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+qg_status qgemv_q4k(const float* x, int64_t ldx, const uint8_t* w, float* y, int64_t ldy,
+                    int64_t M, int64_t N, int64_t K, void* stream) {
+  static const char fn[] = "qgemv_q4k";
+  if (!x || !w || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w and y are required", fn);
+  return q4k_common(fn, x, ldx, w, nullptr, y, ldy, M, N, K, stream);
+}
+
+qg_status qgemv_q4k_dsc(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
+                        int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+  static const char fn[] = "qgemv_q4k_dsc";
+  if (!x || !w || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w and y are required", fn);
+  if (!dsc) return fail(QG_ERR_NULL_POINTER, "%s: dsc plane is NULL (no silent fallback)", fn);
+  return q4k_common(fn, x, ldx, w, dsc, y, ldy, M, N, K, stream);
+}
+
+qg_status gemv_bf16(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
+                    int64_t ldy, int32_t y_type, int64_t M, int64_t N, int64_t K, void* stream) {
+  static const char fn[] = "gemv_bf16";
+  if (!x || !w || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w and y are required", fn);
+  if (qg_status s = check_mnk(fn, M, N, K)) return s;
+  if (!valid_out_dtype(y_type)) return fail(QG_ERR_UNSUPPORTED, "%s: y_type %d", fn, y_type);
+  if (qg_status s = check_ld(fn, "ldx", ldx, K)) return s;
+  if (qg_status s = check_ld(fn, "ldw", ldw, K)) return s;
+  if (qg_status s = check_ld(fn, "ldy", ldy, N)) return s;
+  if (N > 0 && ((N - 1) * ldw + K) * 2 >= kMaxTensorBytes)
+    return fail(QG_ERR_UNSUPPORTED, "%s: w spans 4 GiB or more (kernels use 32-bit offsets)", fn);
+  if (!aligned(x, 2) || !aligned(w, 2))
+    return fail(QG_ERR_MISALIGNED, "%s: x and w must be 2-byte aligned", fn);
+  const int ysz = dtype_size(y_type);
+  if (!aligned(y, ysz)) return fail(QG_ERR_MISALIGNED, "%s: y must be %d-byte aligned", fn, ysz);
+  const Range ry = range_of(y, ((M - 1) * ldy + N) * ysz);
+  if (N > 0 && (overlap(ry, range_of(x, ((M - 1) * ldx + K) * 2)) ||
+                overlap(ry, range_of(w, ((N - 1) * ldw + K) * 2))))
+    return fail(QG_ERR_ALIAS, "%s: y overlaps an input", fn);
+  if (N == 0) return ok();
+  return hip_status(qg::launch_bf16_gemv(x, ldx, w, ldw, y, ldy, y_type, (int)M, (int)N, (int)K,
+                                         static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t q4k_dsc_plane_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K < 1 || K % 256 != 0) return 0;
+  return (size_t)N * (size_t)K / 4;
+}
+
+qg_status q4k_build_dsc_plane(const uint8_t* w, float* dsc_out, int64_t N, int64_t K,
+                              void* stream) {
+  static const char fn[] = "q4k_build_dsc_plane";
+  if (!w || !dsc_out) return fail(QG_ERR_NULL_POINTER, "%s: w and dsc_out are required", fn);
+  if (N < 0 || K < 1 || K % 256 != 0)
+    return fail(QG_ERR_BAD_SHAPE, "%s: N = %lld, K = %lld (need N >= 0, K a positive multiple of 256)",
+                fn, (long long)N, (long long)K);
+  if (N > INT32_MAX || K > INT32_MAX) return fail(QG_ERR_BAD_SHAPE, "%s: N or K exceeds 2^31-1", fn);
+  if (!aligned(w, 16) || !aligned(dsc_out, 16))
+    return fail(QG_ERR_MISALIGNED, "%s: w and dsc_out must be 16-byte aligned", fn);
+  if (N * (K / 256) * 144 >= kMaxTensorBytes)
+    return fail(QG_ERR_UNSUPPORTED, "%s: w is 4 GiB or larger (kernels use 32-bit offsets)", fn);
+  if (N > 0 && overlap(range_of(dsc_out, N * K / 4), range_of(w, N * (K / 256) * 144)))
+    return fail(QG_ERR_ALIAS, "%s: dsc_out overlaps w", fn);
+  if (N == 0) return ok();
+  return hip_status(qg::launch_q4k_build_plane(w, dsc_out, (int)N, (int)K,
+                                               static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,102 @@
+// qgemv_device.h -- device-side helpers shared by the gfx950 GEMV kernels.
+//
+// Everything here is CDNA4 code: 64-wide wavefronts, packed-f16 VOP3P math,
+// v_dot2 instructions, DPP/bpermute cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts)
+constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, 32 CUs each
+
+template <typename T, typename U>
+__device__ __forceinline__ T bitcast(U u) {
+  static_assert(sizeof(T) == sizeof(U), "size");
+  return __builtin_bit_cast(T, u);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)bitcast<_Float16>((uint16_t)bits16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// Workgroups are handed to the XCDs round-robin (workgroup id mod 8).  Give
+// each XCD one contiguous range of tiles instead, so that tiles which share
+// cache lines (neighbouring rows of a plane, the tail of one row and the head
+// of the next) are served by the same L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_tile(int bid, int n) {
+  const int q = n / kXcds, r = n % kXcds;
+  const int xcd = bid % kXcds, idx = bid / kXcds;
+  return xcd * q + (xcd < r ? xcd : r) + idx;
+}
+
+// A 32-bit constant the compiler must keep in a VGPR.  gfx9 VOP3 encodings
+// cannot carry a literal, so (word & mask) | magic only becomes a single
+// v_and_or_b32 when one of the two constants already lives in a register.
+__device__ __forceinline__ uint32_t vreg_const(uint32_t c) {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(c));
+  return v;
+}
+
+// DPP lane permutes within a row of 16 lanes.
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within 16
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64);
+// every lane of the group receives the group total.  Steps inside a 16-lane
+// row use DPP (fused into v_add_f32_dpp); larger groups finish with shuffles.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp_f32<kDppXor1>(v);
+  if constexpr (G >= 4) v += dpp_f32<kDppXor2>(v);
+  if constexpr (G >= 8) v += dpp_f32<kDppHalfMirror>(v);
+  if constexpr (G >= 16) v += dpp_f32<kDppMirror>(v);
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// Round-to-nearest-even store of an fp32 result in the output type.
+// y_type: 0 = fp16, 1 = bf16, 2 = fp32 (the qg_dtype values).
+__device__ __forceinline__ void store_out(void* y, int64_t idx, float v, int y_type) {
+  if (y_type == 0)
+    static_cast<_Float16*>(y)[idx] = (_Float16)v;
+  else if (y_type == 1)
+    static_cast<__bf16*>(y)[idx] = (__bf16)v;
+  else
+    static_cast<float*>(y)[idx] = v;
+}
+
+// 128-bit weight-stream load.  The weights are read exactly once per call, so
+// they are loaded non-temporally: they should not displace x, the scales or
+// the output in the caches.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float2 load_stream8f(const float2* p) {
+  const f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+  return make_float2(v.x, v.y);
+}
+
+}  // namespace qg

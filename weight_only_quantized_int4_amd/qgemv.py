@@ -1,0 +1,145 @@
+"""ctypes binding of libqgemv.so -- argument marshalling only.
+
+Every function takes torch tensors, checks nothing that the C library does not
+check itself beyond what ctypes needs (dtype -> pointer type, shapes -> sizes,
+strides -> leading dimensions), passes ``data_ptr()`` and the current HIP
+stream, and raises ``QgemvError`` with the library's own message on a non-OK
+status.  All compute happens in the HIP kernels; if the library is missing the
+import of a function fails loudly -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+
+QG_F16, QG_BF16, QG_F32 = 0, 1, 2
+_OUT_TYPES = {torch.float16: QG_F16, torch.bfloat16: QG_BF16, torch.float32: QG_F32}
+
+
+class QgemvError(RuntimeError):
+    """A libqgemv entry point returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int, name: str, detail: str):
+        super().__init__(f"{fn}: {name} ({status}): {detail}")
+        self.status = status
+        self.status_name = name
+        self.detail = detail
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libqgemv.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I64, I32, St = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    sigs = {
+        "qgemv_int4_blockwise": (St, [P, I64, P, P, P, P, I64, I32, I64, I64, I64, I32, P]),
+        "qgemv_q4k": (St, [P, I64, P, P, I64, I64, I64, I64, P]),
+        "qgemv_q4k_dsc": (St, [P, I64, P, P, P, I64, I64, I64, I64, P]),
+        "gemv_bf16": (St, [P, I64, P, I64, P, I64, I32, I64, I64, I64, P]),
+        "q4k_dsc_plane_bytes": (ctypes.c_size_t, [I64, I64]),
+        "q4k_build_dsc_plane": (St, [P, P, I64, I64, P]),
+        "qg_status_string": (ctypes.c_char_p, [St]),
+        "qg_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        L = load_library()
+        raise QgemvError(fn, status, L.qg_status_string(status).decode(),
+                         L.qg_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ld(t: torch.Tensor) -> int:
+    """Leading dimension of a row-major 2-D tensor (unit stride in the last dim)."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with unit stride in its last dimension")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+def qgemv_int4_blockwise(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
+                         zero_points: Optional[torch.Tensor], y: torch.Tensor,
+                         block_size: int, stream=None) -> torch.Tensor:
+    """y[M,N] = x[M,K] . dequant(w)^T.  x fp16 [M,K]; w uint8 [N,K/2]; scales
+    fp16 [N,K/bs]; zero_points uint8 [N,ceil(K/bs/2)] or None; y fp16/bf16/fp32 [M,N]."""
+    M, K = x.shape
+    N = w.shape[0]
+    _check("qgemv_int4_blockwise", load_library().qgemv_int4_blockwise(
+        _ptr(x), _ld(x), _ptr(w), _ptr(scales), _ptr(zero_points), _ptr(y), _ld(y),
+        _OUT_TYPES[y.dtype], M, N, K, block_size, _stream(stream)))
+    return y
+
+
+def qgemv_q4k(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """q4_K GEMV.  x fp32 [M,K]; w uint8 [N, K/256*144]; y fp32 [M,N]."""
+    M, K = x.shape
+    N = w.shape[0]
+    _check("qgemv_q4k", load_library().qgemv_q4k(
+        _ptr(x), _ld(x), _ptr(w), _ptr(y), _ld(y), M, N, K, _stream(stream)))
+    return y
+
+
+def qgemv_q4k_dsc(x: torch.Tensor, w: torch.Tensor, dsc: Optional[torch.Tensor],
+                  y: torch.Tensor, stream=None) -> torch.Tensor:
+    """q4_K GEMV with (dv, mv) read from the W_dsc plane (fp32 [(K/32)*N, 2])."""
+    M, K = x.shape
+    N = w.shape[0]
+    _check("qgemv_q4k_dsc", load_library().qgemv_q4k_dsc(
+        _ptr(x), _ld(x), _ptr(w), _ptr(dsc), _ptr(y), _ld(y), M, N, K, _stream(stream)))
+    return y
+
+
+def gemv_bf16(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """y[M,N] = x[M,K] . w[N,K]^T in bf16 (any K, any 2-byte offset)."""
+    M, K = x.shape
+    N = w.shape[0]
+    _check("gemv_bf16", load_library().gemv_bf16(
+        _ptr(x), _ld(x), _ptr(w), _ld(w), _ptr(y), _ld(y), _OUT_TYPES[y.dtype], M, N, K,
+        _stream(stream)))
+    return y
+
+
+def q4k_dsc_plane_bytes(N: int, K: int) -> int:
+    return int(load_library().q4k_dsc_plane_bytes(N, K))
+
+
+def q4k_build_dsc_plane(w: torch.Tensor, dsc_out: torch.Tensor, N: int, K: int,
+                        stream=None) -> torch.Tensor:
+    """Load-time repack of raw q4_K weights into the chunk-major W_dsc plane."""
+    _check("q4k_build_dsc_plane", load_library().q4k_build_dsc_plane(
+        _ptr(w), _ptr(dsc_out), N, K, _stream(stream)))
+    return dsc_out
