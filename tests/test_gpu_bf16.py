@@ -96,12 +96,18 @@ def test_invariants_and_stream():
     base = y_host(y)
     q.gemv_bf16(xd, wd, y)
     assert np.array_equal(base, y_host(y))
+    # v_dot2_f32_bf16 is not sign-symmetric in its rounding on gfx950 (a
+    # probe of the instruction against exact arithmetic shows ~1% of random
+    # cases off round-to-nearest), so y(-x) = -y(x) holds to the tolerance,
+    # not bitwise.
     q.gemv_bf16(-xd, wd, y)
-    assert np.array_equal(y_host(y), -base)
+    yr, S = _ref(p, 4)
+    assert_accept(-y_host(y), yr, S, "f32", "bf16 y(-x)")
+    assert np.max(np.abs(y_host(y) + base)) <= 1e-5 * np.max(np.abs(base))
     # the call is enqueued on the caller's current stream
     s = torch.cuda.Stream()
-    torch.cuda.synchronize()
     y2 = torch.zeros((4, 1536), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
     with torch.cuda.stream(s):
         torch.cuda._sleep(50_000_000)
         q.gemv_bf16(xd, wd, y2)

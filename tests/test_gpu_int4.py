@@ -178,12 +178,21 @@ def test_invariants():
     q.qgemv_int4_blockwise(f16_dev(p.x[:M]), to_dev(p.w[perm]), f16_dev(p.scales[perm]),
                            to_dev(p.zp[perm]), yp, bs)
     assert np.array_equal(y_host(yp), base[:, perm])
-    # row m of an M = 8 call equals the M = 1 call on that row (x fits LDS in one pass)
-    for m in (0, 5):
+    # row independence: a row of an M = 2 call equals the M = 1 call on that row
+    # bitwise (same lane mapping and summation order); a row of the M = 8 call
+    # (another lanes-per-row choice) agrees to the tolerance
+    yr, S = int4_ref(N, K, bs, True, 91)
+    y2 = torch.empty((2, N), dtype=torch.float32, device=DEV)
+    q.qgemv_int4_blockwise(f16_dev(p.x[4:6]), to_dev(p.w), f16_dev(p.scales), to_dev(p.zp), y2, bs)
+    y2 = y_host(y2)
+    for m in (4, 5):
         y1 = torch.empty((1, N), dtype=torch.float32, device=DEV)
         q.qgemv_int4_blockwise(f16_dev(p.x[m:m + 1]), to_dev(p.w), f16_dev(p.scales),
                                to_dev(p.zp), y1, bs)
-        assert np.array_equal(y_host(y1)[0], base[m])
+        y1 = y_host(y1)[0]
+        assert np.array_equal(y1, y2[m - 4])
+        assert_accept(y1[None], base[m][None], S[m][None] + 0 * yr[m][None], "f32", "row m")
+        assert_accept(base[m][None], yr[m][None], S[m][None], "f32", "row m of M=8")
 
 
 def test_empty_and_rejected_calls_on_device():

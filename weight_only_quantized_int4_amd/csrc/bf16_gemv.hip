@@ -48,6 +48,7 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
 
+#pragma unroll 1
   for (int kc = 0; kc < K; kc += KC) {
     const int kn = min(KC, K - kc);
     const int P = kn >> 3;
@@ -63,6 +64,7 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
       xs[m * G + i] = *reinterpret_cast<const uint4*>(x + m * ldx + kc + 8 * i);
     }
     __syncthreads();
+#pragma unroll 1
     for (int p = j; p < P; p += LPR) {
       uint4 nxt[R];
       const bool more = p + LPR < P;
@@ -121,6 +123,7 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_general(
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.f;
 
+#pragma unroll 1
   for (int kc = 0; kc < K; kc += KC) {
     const int kn = min(KC, K - kc);
     const int ext = min(kn + 8, K - kc);

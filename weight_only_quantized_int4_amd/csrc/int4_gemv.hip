@@ -117,6 +117,7 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_kernel(
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
 
+#pragma unroll 1
   for (int kc = 0; kc < K; kc += KC) {
     const int kn = min(KC, K - kc);
     const int P = kn >> 5;
@@ -146,6 +147,7 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_kernel(
     }
     __syncthreads();
 
+#pragma unroll 1
     for (int p = j; p < P; p += LPR) {
       // Prefetch the next piece while this one is computed.
       Piece<R> nxt;
@@ -206,18 +208,170 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_kernel(
     }
 }
 
+// Persistent variant, used whenever all of x fits in LDS: one resident round
+// of workgroups, each staging x once and then streaming an equal, contiguous
+// share of row tiles.  A lane's work is a flat sequence of (tile, piece)
+// items with a one-item register prefetch that runs across tile boundaries;
+// when a tile's last piece is done its rows are reduced and stored.
+template <int M, int LPR, int R, bool ZP>
+__global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zp, int zrow,
+    void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int bs_log2, int ntiles,
+    int x_vec16) {
+  extern __shared__ uint4 xs[];  // [M][K/32][5]: 4 permuted groups of 8 halves + pad
+  constexpr int S = kBlock / LPR;  // row slots per workgroup
+  constexpr int RT = S * R;        // rows per tile
+  const int tid = threadIdx.x;
+  const int slot = tid / LPR;
+  const int j = tid % LPR;
+  const int b = xcd_tile(blockIdx.x, gridDim.x);
+  const int t_begin = (int)((int64_t)b * ntiles / gridDim.x);
+  const int t_end = (int)((int64_t)(b + 1) * ntiles / gridDim.x);
+  const int nb = K >> bs_log2;
+  const int P = K >> 5;
+  const int PPI = (P + LPR - 1) / LPR;  // pieces per lane per tile
+  const int PS = P * 5;
+  const uint32_t magic = vreg_const(0x64006400u);
+
+  auto load = [&](Piece<R>& st, int tile, int it) {
+    int p = j + LPR * it;
+    p = p < P ? p : P - 1;  // idle lanes of a ragged last stride re-read a valid piece
+    const uint32_t blk = (uint32_t)((p << 5) >> bs_log2);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int row = tile * RT + i * S + slot;
+      const uint32_t nl = (uint32_t)(row < N ? row : N - 1);
+      st.w[i] = load_stream16(w + (nl * (uint32_t)(K >> 1) + (uint32_t)p * 16u));
+      st.s[i] = scales[nl * (uint32_t)nb + blk];
+      st.z[i] = ZP ? zp[nl * (uint32_t)zrow + (blk >> 1)] : 0x88u;
+    }
+  };
+
+  const int nitems = (t_end - t_begin) * PPI;
+  Piece<R> cur;
+  if (nitems > 0) load(cur, t_begin, 0);
+
+  const int groups = K >> 3;
+  for (int t = tid; t < M * groups; t += kBlock) {
+    const int m = t / groups;
+    const int gi = t - m * groups;
+    const uint16_t* src = x + m * ldx + gi * 8;
+    uint32_t h[8];
+    if (x_vec16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      h[0] = v.x & 0xFFFFu; h[1] = v.x >> 16; h[2] = v.y & 0xFFFFu; h[3] = v.y >> 16;
+      h[4] = v.z & 0xFFFFu; h[5] = v.z >> 16; h[6] = v.w & 0xFFFFu; h[7] = v.w >> 16;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = src[e];
+    }
+    xs[m * PS + (gi >> 2) * 5 + (gi & 3)] = make_uint4(
+        h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16), h[3] | (h[7] << 16));
+  }
+  __syncthreads();
+
+  float acc[R][M];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
+
+  int tile = t_begin, it = 0;
+#pragma unroll 1
+  for (int u = 0; u < nitems; ++u) {
+    int ntile = tile, nit = it + 1;
+    if (nit == PPI) {
+      nit = 0;
+      ++ntile;
+    }
+    Piece<R> nxt;
+    const bool more = u + 1 < nitems;
+    if (more) load(nxt, ntile, nit);
+
+    const int p = j + LPR * it;
+    if (p < P) {
+      const int zsh = (((p << 5) >> bs_log2) & 1) << 2;
+      float sc[R];
+      uint32_t blo[R], bhi[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        sc[i] = f16_to_f32(cur.s[i]);
+        const uint32_t z = (cur.z[i] >> zsh) & 15u;
+        blo[i] = (0xE400u + z) * 0x00010001u;         // -(1024 + zp) in both halves
+        bhi[i] = (0xD400u + (z << 4)) * 0x00010001u;  // -(64 + zp) in both halves
+      }
+      float part[R][M];
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m) part[i][m] = 0.f;
+      const uint4* xp = xs + p * 5;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint4 xv[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xv[m] = xp[m * PS + d];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const Pairs8 q = unpack8(word_of(cur.w[i], d), magic, blo[i], bhi[i]);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float t = part[i][m];
+            t = __builtin_amdgcn_fdot2(q.a, bitcast<f16x2>(xv[m].x), t, false);
+            t = __builtin_amdgcn_fdot2(q.b, bitcast<f16x2>(xv[m].y), t, false);
+            t = __builtin_amdgcn_fdot2(q.c, bitcast<f16x2>(xv[m].z), t, false);
+            t = __builtin_amdgcn_fdot2(q.d, bitcast<f16x2>(xv[m].w), t, false);
+            part[i][m] = t;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[i][m] = __builtin_fmaf(sc[i], part[i][m], acc[i][m]);
+    }
+
+    if (it == PPI - 1) {  // tile finished (uniform across the workgroup)
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int row = tile * RT + i * S + slot;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const float v = group_sum<LPR>(acc[i][m]);
+          acc[i][m] = 0.f;
+          if (j == 0 && row < N) store_out(y, m * ldy + row, v, y_type);
+        }
+      }
+    }
+    if (more) cur = nxt;
+    tile = ntile;
+    it = nit;
+  }
+}
+
 template <int M, int LPR, int R>
 hipError_t launch_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* scales,
                       const uint8_t* zp, void* y, int64_t ldy, int y_type, int N, int K,
                       int block_size, hipStream_t stream) {
   constexpr int RT = (kBlock / LPR) * R;
-  const int grid = (N + RT - 1) / RT;
-  // x takes 80 bytes of LDS per 32 elements and row.
-  int KC = (kLdsBudget / (80 * M)) * 32;
-  if (KC > K) KC = K;
   const int bs_log2 = __builtin_ctz((unsigned)block_size);
   const int zrow = ((K / block_size) + 1) / 2;
   const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
+  const int ntiles = (N + RT - 1) / RT;
+  // x takes 80 bytes of LDS per 32 elements and row.
+  const size_t full = (size_t)M * (K / 32) * 80;
+  if (full <= (size_t)kLdsBudget) {
+    auto kern = zp ? int4_gemv_persistent<M, LPR, R, true> : int4_gemv_persistent<M, LPR, R, false>;
+    const int cap = resident_workgroups(kern, kBlock, full);
+    const int grid = ntiles < cap ? ntiles : cap;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), full, stream, x, ldx, w, scales, zp, zrow,
+                       y, ldy, y_type, N, K, bs_log2, ntiles, x_vec16);
+    return hipGetLastError();
+  }
+  const int grid = ntiles;
+  int KC = (kLdsBudget / (80 * M)) * 32;
+  if (KC > K) KC = K;
   const size_t shmem = (size_t)M * (KC / 32) * 80;
   if (zp)
     hipLaunchKernelGGL((int4_gemv_kernel<M, LPR, R, true>), dim3(grid), dim3(kBlock), shmem,
@@ -234,14 +388,23 @@ template <int M>
 hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* scales,
                     const uint8_t* zp, void* y, int64_t ldy, int y_type, int N, int K,
                     int block_size, hipStream_t stream) {
+  // Lanes per row (measured on the 151936 x 4096 lm_head shape): 32 is best at
+  // small M, 8 at large M (more rows share each x read).  Take the first
+  // preference that divides the row's piece count, so no lane idles in the
+  // last stride of a row.
   const int P = K / 32;  // 16-byte pieces per row
-  // Lanes per row: a divisor of the piece count when possible so that no
-  // lane idles in the last stride of a row.
-  const bool lpr8 = (P % 16 != 0) && (P % 8 == 0);
-  constexpr int R = 2;
-  if (lpr8)
-    return launch_cfg<M, 8, R>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
-  return launch_cfg<M, 16, R>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+  constexpr int pref[3] = {M <= 2 ? 32 : 8, 16, M <= 2 ? 8 : 32};
+  int lpr = pref[0];
+  for (int c : pref)
+    if (P % c == 0) {
+      lpr = c;
+      break;
+    }
+  if (lpr == 32)
+    return launch_cfg<M, 32, 2>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+  if (lpr == 16)
+    return launch_cfg<M, 16, 2>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+  return launch_cfg<M, 8, 2>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
 }
 
 }  // namespace

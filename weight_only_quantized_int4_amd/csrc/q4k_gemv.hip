@@ -16,9 +16,11 @@
 //    (the same structural argument the page makes for its two kernel
 //    instances).
 //  * A "piece" is 32 quant bytes of one super-block = chunks 2g and 2g+1
-//    (64 weights).  A group of LPR lanes (LPR a multiple of 4) owns a row; lane
-//    j always has the same g = j % 4, so its half-pair of the 6-bit decode is
-//    loop-invariant and branch-free.
+//    (64 weights).  A whole wavefront owns a row (LPR = 64 lanes); lane j
+//    always has the same g = j % 4, so its half-pair of the 6-bit decode is
+//    loop-invariant and branch-free.  A K = 4096 row is 64 pieces, one per
+//    lane, so every lane's 48 bytes are in flight at once; a workgroup of 16
+//    wavefronts covers 16 rows and shares one staged copy of x.
 //  * Rank-1 factorisation per chunk: sum_l (dv*q_l + mv) x_l is evaluated as
 //    dv * (sum_l q_l x_l) + mv * (sum_l x_l).  The chunk sums of x are computed
 //    once per workgroup while x is staged in LDS, so the inner loop spends one
@@ -26,6 +28,9 @@
 //    x this still reproduces w = RN(dv*q + mv) bit-exactly.
 //  * Quants are converted with the fp16 1024.0 mantissa trick (exact), as in
 //    the int4 kernel.
+//  * Weights are read with plain (cached) loads: a super-block's header and
+//    quants share cache lines and are read by different instructions
+//    (measured faster than non-temporal loads here).
 //  * x lives in LDS as fp32 with 4 floats of padding after every 64: the
 //    lanes of a row read pieces 272 bytes apart, so their 16-byte LDS reads
 //    fall in distinct banks (without the padding all of them would hit the
@@ -70,8 +75,8 @@ struct Q4kPiece {
   float2 ea, eb;  // plane entries of chunks 2g and 2g+1 (DSC = true)
 };
 
-template <int M, int LPR, bool DSC>
-__global__ __launch_bounds__(kBlock) void q4k_gemv_kernel(
+template <int M, int LPR, int NT, bool DSC>
+__global__ __launch_bounds__(NT) void q4k_gemv_kernel(
     const float* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const float2* __restrict__ dsc, float* __restrict__ y, int64_t ldy, int N, int K, int KC,
     int x_vec16) {
@@ -81,7 +86,7 @@ __global__ __launch_bounds__(kBlock) void q4k_gemv_kernel(
   float* xs = smem;                 // [M][KC/64][68]
   float* sx = smem + M * XSTR;      // [M][KC/32] chunk sums of x
   const int KC32 = KC >> 5;
-  constexpr int S = kBlock / LPR;
+  constexpr int S = NT / LPR;
   const int tid = threadIdx.x;
   const int slot = tid / LPR;
   const int j = tid % LPR;
@@ -100,14 +105,14 @@ __global__ __launch_bounds__(kBlock) void q4k_gemv_kernel(
 
   auto load = [&](Q4kPiece& st, int sb) {
     const uint32_t bo = wo + (uint32_t)sb * kQ4kBlockBytes;
-    st.q0 = load_stream16(w + (bo + 16u + 32u * g));
-    st.q1 = load_stream16(w + (bo + 32u + 32u * g));
+    st.q0 = load16(w + (bo + 16u + 32u * g));
+    st.q1 = load16(w + (bo + 32u + 32u * g));
     if constexpr (DSC) {
       const uint32_t c = (uint32_t)sb * 8u + 2u * g;
-      st.ea = load_stream8f(dsc + (c * (uint32_t)N + nl));
-      st.eb = load_stream8f(dsc + ((c + 1u) * (uint32_t)N + nl));
+      st.ea = load8f(dsc + (c * (uint32_t)N + nl));
+      st.eb = load8f(dsc + ((c + 1u) * (uint32_t)N + nl));
     } else {
-      st.h = load_stream16(w + bo);
+      st.h = load16(w + bo);
     }
   };
 
@@ -115,6 +120,7 @@ __global__ __launch_bounds__(kBlock) void q4k_gemv_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.f;
 
+#pragma unroll 1
   for (int kc = 0; kc < K; kc += KC) {
     const int kn = min(KC, K - kc);
     const int P = kn >> 6;  // (super-block, g) pieces in this chunk
@@ -126,21 +132,21 @@ __global__ __launch_bounds__(kBlock) void q4k_gemv_kernel(
     __syncthreads();
     if (x_vec16) {
       const int v4 = kn >> 2;
-      for (int t = tid; t < M * v4; t += kBlock) {
+      for (int t = tid; t < M * v4; t += NT) {
         const int m = t / v4, i = t - m * v4;
         const int e = 4 * i;
         *reinterpret_cast<float4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) =
             *reinterpret_cast<const float4*>(x + m * ldx + kc + e);
       }
     } else {
-      for (int t = tid; t < M * kn; t += kBlock) {
+      for (int t = tid; t < M * kn; t += NT) {
         const int m = t / kn, i = t - m * kn;
         xs[m * XSTR + (i >> 6) * 68 + (i & 63)] = x[m * ldx + kc + i];
       }
     }
     __syncthreads();
     const int nch = kn >> 5;
-    for (int t = tid; t < M * nch; t += kBlock) {
+    for (int t = tid; t < M * nch; t += NT) {
       const int m = t / nch, c = t - m * nch;
       const float* src = xs + m * XSTR + (c >> 1) * 68 + 32 * (c & 1);
       float s = 0.f;
@@ -150,6 +156,7 @@ __global__ __launch_bounds__(kBlock) void q4k_gemv_kernel(
     }
     __syncthreads();
 
+#pragma unroll 1
     for (int p = j; p < P; p += LPR) {
       Q4kPiece nxt;
       const bool more = p + LPR < P;
@@ -222,6 +229,176 @@ __global__ __launch_bounds__(kBlock) void q4k_gemv_kernel(
   }
 }
 
+// Persistent variant, used whenever x and its chunk sums fit in LDS: one
+// resident round of workgroups; each stages x once and splits an equal,
+// contiguous share of rows among its wavefronts.  A wavefront owns one row at
+// a time (LPR = 64) and walks a flat sequence of (row, piece) items with a
+// one-item prefetch that crosses row boundaries.
+template <int M, int NT, bool DSC>
+__global__ __launch_bounds__(NT) void q4k_gemv_persistent(
+    const float* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
+    const float2* __restrict__ dsc, float* __restrict__ y, int64_t ldy, int N, int K,
+    int x_vec16) {
+  constexpr int NW = NT / kWave;  // wavefronts (rows in flight) per workgroup
+  extern __shared__ float smem[];
+  const int XSTR = (K >> 6) * 68;  // floats per x row in LDS (64 + 4 pad per piece)
+  float* xs = smem;                // [M][K/64][68]
+  float* sx = smem + M * XSTR;     // [M][K/32] chunk sums of x
+  const int K32 = K >> 5;
+  const int tid = threadIdx.x;
+  const int wv = tid / kWave;
+  const int j = tid % kWave;
+  const int g = j & 3;
+  const int b = xcd_tile(blockIdx.x, gridDim.x);
+  const int r_begin = (int)((int64_t)b * N / gridDim.x);
+  const int r_end = (int)((int64_t)(b + 1) * N / gridDim.x);
+  const int nsb = K >> 8;
+  const int P = K >> 6;                  // pieces per row
+  const int PPI = (P + kWave - 1) / kWave;  // pieces per lane per row
+  const int span = r_end - r_begin - wv;
+  const int nrows = span > 0 ? (span + NW - 1) / NW : 0;  // rows of this wavefront
+  const int nitems = nrows * PPI;
+
+  const uint32_t magic = vreg_const(0x64006400u);
+  const f16x2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const f16x2 m64 = {(_Float16)-64.0f, (_Float16)-64.0f};
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+
+  auto load = [&](Q4kPiece& st, int row, int it) {
+    int p = j + kWave * it;
+    p = p < P ? p : P - 1;  // idle lanes of a ragged last stride re-read a valid piece
+    const uint32_t sb = (uint32_t)(p >> 2);
+    const uint32_t bo = ((uint32_t)row * (uint32_t)nsb + sb) * (uint32_t)kQ4kBlockBytes;
+    st.q0 = load16(w + (bo + 16u + 32u * g));
+    st.q1 = load16(w + (bo + 32u + 32u * g));
+    if constexpr (DSC) {
+      const uint32_t c = sb * 8u + 2u * g;
+      st.ea = load8f(dsc + (c * (uint32_t)N + (uint32_t)row));
+      st.eb = load8f(dsc + ((c + 1u) * (uint32_t)N + (uint32_t)row));
+    } else {
+      st.h = load16(w + bo);
+    }
+  };
+
+  Q4kPiece cur;
+  if (nitems > 0) load(cur, r_begin + wv, 0);
+
+  // Stage x; the chunk sums come out of the same pass when x is 16-byte
+  // aligned (8 consecutive lanes hold one 32-element chunk).
+  if (x_vec16) {
+    const int v4 = K >> 2;
+    for (int t = tid; t < M * v4; t += NT) {
+      const int m = t / v4, i = t - m * v4;
+      const int e = 4 * i;
+      const float4 v = *reinterpret_cast<const float4*>(x + m * ldx + e);
+      *reinterpret_cast<float4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) = v;
+      const float part = group_sum<8>((v.x + v.y) + (v.z + v.w));
+      if ((i & 7) == 0) sx[m * K32 + (i >> 3)] = part;
+    }
+    __syncthreads();
+  } else {
+    for (int t = tid; t < M * K; t += NT) {
+      const int m = t / K, i = t - m * K;
+      xs[m * XSTR + (i >> 6) * 68 + (i & 63)] = x[m * ldx + i];
+    }
+    __syncthreads();
+    for (int t = tid; t < M * K32; t += NT) {
+      const int m = t / K32, c = t - m * K32;
+      const float* src = xs + m * XSTR + (c >> 1) * 68 + 32 * (c & 1);
+      float sum = 0.f;
+#pragma unroll
+      for (int l = 0; l < 32; ++l) sum += src[l];
+      sx[m * K32 + c] = sum;
+    }
+    __syncthreads();
+  }
+
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+  int row = r_begin + wv, it = 0;
+#pragma unroll 1
+  for (int u = 0; u < nitems; ++u) {
+    int nrow = row, nit = it + 1;
+    if (nit == PPI) {
+      nit = 0;
+      nrow += NW;
+    }
+    Q4kPiece nxt;
+    const bool more = u + 1 < nitems;
+    if (more) load(nxt, nrow, nit);
+
+    const int p = j + kWave * it;
+    if (p < P) {
+      float dva, mva, dvb, mvb;
+      if constexpr (DSC) {
+        dva = cur.ea.x; mva = cur.ea.y; dvb = cur.eb.x; mvb = cur.eb.y;
+      } else {
+        uint32_t s2, m2;
+        scale_min_pair(cur.h.y, cur.h.z, cur.h.w, g, s2, m2);
+        const float d = f16_to_f32(cur.h.x & 0xFFFFu);
+        const float dmin = f16_to_f32(cur.h.x >> 16);
+        dva = d * (float)(s2 & 0xFFu);
+        dvb = d * (float)(s2 >> 8);
+        mva = -(dmin * (float)(m2 & 0xFFu));
+        mvb = -(dmin * (float)(m2 >> 8));
+      }
+      float pa[M], pb[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) pa[m] = pb[m] = 0.f;
+      const float* xa = xs + p * 68;  // chunk 2g; chunk 2g+1 at +32
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t word = t < 4 ? word_of(cur.q0, t) : word_of(cur.q1, t - 4);
+        const uint32_t w8 = word >> 8;
+        const f16x2 A = bitcast<f16x2>((word & 0x000F000Fu) | magic) + m1024;
+        const f16x2 C = bitcast<f16x2>((w8 & 0x000F000Fu) | magic) + m1024;
+        const f16x2 B = __builtin_elementwise_fma(
+            bitcast<f16x2>((word & 0x00F000F0u) | magic), sixteenth, m64);
+        const f16x2 D = __builtin_elementwise_fma(
+            bitcast<f16x2>((w8 & 0x00F000F0u) | magic), sixteenth, m64);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const float4 xa4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 4 * t);
+          const float4 xb4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 32 + 4 * t);
+          float u0 = pa[m], v0 = pb[m];
+          u0 = __builtin_fmaf((float)A.x, xa4.x, u0);
+          u0 = __builtin_fmaf((float)C.x, xa4.y, u0);
+          u0 = __builtin_fmaf((float)A.y, xa4.z, u0);
+          u0 = __builtin_fmaf((float)C.y, xa4.w, u0);
+          v0 = __builtin_fmaf((float)B.x, xb4.x, v0);
+          v0 = __builtin_fmaf((float)D.x, xb4.y, v0);
+          v0 = __builtin_fmaf((float)B.y, xb4.z, v0);
+          v0 = __builtin_fmaf((float)D.y, xb4.w, v0);
+          pa[m] = u0;
+          pb[m] = v0;
+        }
+      }
+      const int ca = 2 * p;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float a = acc[m];
+        a = __builtin_fmaf(dva, pa[m], a);
+        a = __builtin_fmaf(mva, sx[m * K32 + ca], a);
+        a = __builtin_fmaf(dvb, pb[m], a);
+        a = __builtin_fmaf(mvb, sx[m * K32 + ca + 1], a);
+        acc[m] = a;
+      }
+    }
+    if (it == PPI - 1) {  // row finished (uniform across the wavefront)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float v = group_sum<kWave>(acc[m]);
+        acc[m] = 0.f;
+        if (j == 0) y[m * ldy + row] = v;
+      }
+    }
+    if (more) cur = nxt;
+    row = nrow;
+    it = nit;
+  }
+}
+
 // One thread per (super-block sb, row n), n fastest: decode the header once,
 // write the eight (dv, mv) pairs of the super-block.  For a fixed chunk the
 // writes of consecutive threads are consecutive float2s.
@@ -255,23 +432,34 @@ __global__ __launch_bounds__(kBlock) void q4k_plane_kernel(const uint8_t* __rest
   }
 }
 
-template <int M, int LPR>
+template <int M, int LPR, int NT>
 hipError_t launch_cfg(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
                       int64_t ldy, int N, int K, hipStream_t stream) {
-  constexpr int S = kBlock / LPR;
+  const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 4 == 0);
+  const float2* dsc2 = reinterpret_cast<const float2*>(dsc);
+  // x (68 floats per 64 elements) plus its chunk sums (2 floats per 64), fp32.
+  const size_t full = (size_t)M * ((K / 64) * 68 + K / 32) * 4;
+  if (full <= (size_t)kLdsBudget) {
+    auto kern = dsc ? q4k_gemv_persistent<M, NT, true> : q4k_gemv_persistent<M, NT, false>;
+    const int cap = resident_workgroups(kern, NT, full);
+    const int rows_per_wg = NT / kWave;
+    const int want = (N + rows_per_wg - 1) / rows_per_wg;
+    const int grid = want < cap ? want : cap;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), full, stream, x, ldx, w, dsc2, y, ldy, N, K,
+                       x_vec16);
+    return hipGetLastError();
+  }
+  constexpr int S = NT / LPR;
   const int grid = (N + S - 1) / S;
-  // x (68 floats per 64 elements) plus its chunk sums (2 floats per 64), fp32,
-  // within the LDS budget; KC a multiple of 256 (whole super-blocks).
+  // KC a multiple of 256 (whole super-blocks) within the LDS budget.
   int KC = (kLdsBudget / (4 * 70 * M)) * 64 & ~255;
   if (KC > K) KC = K;
   const size_t shmem = (size_t)M * ((KC / 64) * 68 + KC / 32) * 4;
-  const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 4 == 0);
   if (dsc)
-    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, true>), dim3(grid), dim3(kBlock), shmem, stream,
-                       x, ldx, w, reinterpret_cast<const float2*>(dsc), y, ldy, N, K, KC,
-                       x_vec16);
+    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT, true>), dim3(grid), dim3(NT), shmem, stream,
+                       x, ldx, w, dsc2, y, ldy, N, K, KC, x_vec16);
   else
-    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, false>), dim3(grid), dim3(kBlock), shmem, stream,
+    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT, false>), dim3(grid), dim3(NT), shmem, stream,
                        x, ldx, w, nullptr, y, ldy, N, K, KC, x_vec16);
   return hipGetLastError();
 }
@@ -279,7 +467,12 @@ hipError_t launch_cfg(const float* x, int64_t ldx, const uint8_t* w, const float
 template <int M>
 hipError_t launch_m(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
                     int64_t ldy, int N, int K, hipStream_t stream) {
-  return launch_cfg<M, 16>(x, ldx, w, dsc, y, ldy, N, K, stream);
+  // 1024-thread workgroups cap a lane at 128 VGPRs: enough for M = 1 only;
+  // larger M keeps 4 rows per workgroup and the full register file.
+  if constexpr (M == 1)
+    return launch_cfg<M, 64, 1024>(x, ldx, w, dsc, y, ldy, N, K, stream);
+  else
+    return launch_cfg<M, 64, 256>(x, ldx, w, dsc, y, ldy, N, K, stream);
 }
 
 }  // namespace

@@ -94,8 +94,15 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ float2 load_stream8f(const float2* p) {
-  const f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+// Plain 128-bit load, for streams whose cache lines are touched by more than
+// one load instruction (the q4_K header and quants share lines).
+__device__ __forceinline__ uint4 load16(const void* p) {
+  const u32x4 v = *static_cast<const u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float2 load8f(const float2* p) {
+  const f32x2 v = *reinterpret_cast<const f32x2*>(p);
   return make_float2(v.x, v.y);
 }
 

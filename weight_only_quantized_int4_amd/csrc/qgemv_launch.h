@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace qg {
 
 hipError_t launch_int4_gemv(const uint16_t* x, int64_t ldx, const uint8_t* w,
@@ -26,5 +28,43 @@ hipError_t launch_bf16_gemv(const uint16_t* x, int64_t ldx, const uint16_t* w,
 
 // LDS budget per workgroup for staged activations (bytes).
 constexpr int kLdsBudget = 64 * 1024;
+
+// Workgroups of `kernel` that fit on the whole device at once: a host-side
+// occupancy calculation (no GPU work), remembered per (kernel, device, LDS).
+template <typename F>
+inline int resident_workgroups(F kernel, int threads, size_t shmem) {
+  struct Entry {
+    const void* fn;
+    int dev;
+    int threads;
+    size_t shmem;
+    int value;
+  };
+  static std::mutex mu;
+  static Entry table[256];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (table[i].fn == fn && table[i].dev == dev && table[i].threads == threads &&
+          table[i].shmem == shmem)
+        return table[i].value;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, shmem) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 1;
+  const int value = per_cu * cus;
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < 256) table[used++] = Entry{fn, dev, threads, shmem, value};
+  return value;
+}
+
 
 }  // namespace qg
