@@ -209,11 +209,20 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_kernel(
 }
 
 // Persistent variant, used whenever all of x fits in LDS: one resident round
-// of workgroups, each staging x once and then streaming an equal, contiguous
-// share of row tiles.  A lane's work is a flat sequence of (tile, piece)
-// items with a one-item register prefetch that runs across tile boundaries;
-// when a tile's last piece is done its rows are reduced and stored.
-template <int M, int LPR, int R, bool ZP>
+// of workgroups, each staging x once and then streaming row tiles.  A lane's
+// work is a flat sequence of (tile, item) pairs; an item is PB adjacent
+// 16-byte pieces of each of the lane's R rows (PB = 2: 32 contiguous bytes,
+// one zero-point byte for both 32-weight blocks).  A one-item register
+// prefetch runs across tile boundaries; when a tile's last item is done its
+// rows are reduced and stored.
+template <int R, int PB>
+struct Item {
+  uint4 w[R][PB];
+  uint32_t s[R][PB];  // fp16 scale bits per piece
+  uint32_t z[R][PB];  // zero-point byte per piece
+};
+
+template <int M, int LPR, int R, int PB, bool ZP, bool STRIDED>
 __global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zp, int zrow,
@@ -225,31 +234,43 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
   const int tid = threadIdx.x;
   const int slot = tid / LPR;
   const int j = tid % LPR;
-  const int b = xcd_tile(blockIdx.x, gridDim.x);
-  const int t_begin = (int)((int64_t)b * ntiles / gridDim.x);
-  const int t_end = (int)((int64_t)(b + 1) * ntiles / gridDim.x);
+  // Tile order: STRIDED walks tiles b, b+G, b+2G, ... so that the resident
+  // workgroups sweep one compact window of the matrix together; otherwise
+  // workgroup b takes a contiguous range of tiles.
+  const int b = STRIDED ? (int)blockIdx.x : xcd_tile(blockIdx.x, gridDim.x);
+  const int G = (int)gridDim.x;
+  const int t_begin = STRIDED ? b : (int)((int64_t)b * ntiles / G);
+  const int t_end = STRIDED ? ntiles : (int)((int64_t)(b + 1) * ntiles / G);
+  const int t_step = STRIDED ? G : 1;
+  const int my_tiles = STRIDED ? (ntiles - b + G - 1) / G : t_end - t_begin;
   const int nb = K >> bs_log2;
-  const int P = K >> 5;
-  const int PPI = (P + LPR - 1) / LPR;  // pieces per lane per tile
+  const int P = K >> 5;                              // pieces per row
+  const int PPI = (P + LPR * PB - 1) / (LPR * PB);   // items per lane per tile
   const int PS = P * 5;
   const uint32_t magic = vreg_const(0x64006400u);
 
-  auto load = [&](Piece<R>& st, int tile, int it) {
-    int p = j + LPR * it;
-    p = p < P ? p : P - 1;  // idle lanes of a ragged last stride re-read a valid piece
-    const uint32_t blk = (uint32_t)((p << 5) >> bs_log2);
+  auto load = [&](Item<R, PB>& st, int tile, int it) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int row = tile * RT + i * S + slot;
       const uint32_t nl = (uint32_t)(row < N ? row : N - 1);
-      st.w[i] = load_stream16(w + (nl * (uint32_t)(K >> 1) + (uint32_t)p * 16u));
-      st.s[i] = scales[nl * (uint32_t)nb + blk];
-      st.z[i] = ZP ? zp[nl * (uint32_t)zrow + (blk >> 1)] : 0x88u;
+      const uint32_t wrow = nl * (uint32_t)(K >> 1);
+      const uint32_t srow = nl * (uint32_t)nb;
+      const uint32_t zr = nl * (uint32_t)zrow;
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        int p = PB * (j + LPR * it) + q;
+        p = p < P ? p : P - 1;  // idle lanes of a ragged last stride re-read a valid piece
+        const uint32_t blk = (uint32_t)((p << 5) >> bs_log2);
+        st.w[i][q] = load_stream16(w + (wrow + (uint32_t)p * 16u));
+        st.s[i][q] = scales[srow + blk];
+        st.z[i][q] = ZP ? zp[zr + (blk >> 1)] : 0x88u;
+      }
     }
   };
 
-  const int nitems = (t_end - t_begin) * PPI;
-  Piece<R> cur;
+  const int nitems = my_tiles * PPI;
+  Item<R, PB> cur;
   if (nitems > 0) load(cur, t_begin, 0);
 
   const int groups = K >> 3;
@@ -283,53 +304,56 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
     int ntile = tile, nit = it + 1;
     if (nit == PPI) {
       nit = 0;
-      ++ntile;
+      ntile += t_step;
     }
-    Piece<R> nxt;
+    Item<R, PB> nxt;
     const bool more = u + 1 < nitems;
     if (more) load(nxt, ntile, nit);
 
-    const int p = j + LPR * it;
-    if (p < P) {
-      const int zsh = (((p << 5) >> bs_log2) & 1) << 2;
-      float sc[R];
-      uint32_t blo[R], bhi[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        sc[i] = f16_to_f32(cur.s[i]);
-        const uint32_t z = (cur.z[i] >> zsh) & 15u;
-        blo[i] = (0xE400u + z) * 0x00010001u;         // -(1024 + zp) in both halves
-        bhi[i] = (0xD400u + (z << 4)) * 0x00010001u;  // -(64 + zp) in both halves
-      }
-      float part[R][M];
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int m = 0; m < M; ++m) part[i][m] = 0.f;
-      const uint4* xp = xs + p * 5;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint4 xv[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) xv[m] = xp[m * PS + d];
+    for (int q = 0; q < PB; ++q) {
+      const int p = PB * (j + LPR * it) + q;
+      if (p < P) {
+        const int zsh = (((p << 5) >> bs_log2) & 1) << 2;
+        float sc[R];
+        uint32_t blo[R], bhi[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-          const Pairs8 q = unpack8(word_of(cur.w[i], d), magic, blo[i], bhi[i]);
+          sc[i] = f16_to_f32(cur.s[i][q]);
+          const uint32_t z = (cur.z[i][q] >> zsh) & 15u;
+          blo[i] = 0xE400E400u + z * 0x00010001u;          // -(1024 + zp) in both halves
+          bhi[i] = 0xD400D400u + z * 0x00100010u;          // -(64 + zp) in both halves
+        }
+        float part[R][M];
 #pragma unroll
-          for (int m = 0; m < M; ++m) {
-            float t = part[i][m];
-            t = __builtin_amdgcn_fdot2(q.a, bitcast<f16x2>(xv[m].x), t, false);
-            t = __builtin_amdgcn_fdot2(q.b, bitcast<f16x2>(xv[m].y), t, false);
-            t = __builtin_amdgcn_fdot2(q.c, bitcast<f16x2>(xv[m].z), t, false);
-            t = __builtin_amdgcn_fdot2(q.d, bitcast<f16x2>(xv[m].w), t, false);
-            part[i][m] = t;
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int m = 0; m < M; ++m) part[i][m] = 0.f;
+        const uint4* xp = xs + p * 5;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint4 xv[M];
+#pragma unroll
+          for (int m = 0; m < M; ++m) xv[m] = xp[m * PS + d];
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const Pairs8 qq = unpack8(word_of(cur.w[i][q], d), magic, blo[i], bhi[i]);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+              float t = part[i][m];
+              t = __builtin_amdgcn_fdot2(qq.a, bitcast<f16x2>(xv[m].x), t, false);
+              t = __builtin_amdgcn_fdot2(qq.b, bitcast<f16x2>(xv[m].y), t, false);
+              t = __builtin_amdgcn_fdot2(qq.c, bitcast<f16x2>(xv[m].z), t, false);
+              t = __builtin_amdgcn_fdot2(qq.d, bitcast<f16x2>(xv[m].w), t, false);
+              part[i][m] = t;
+            }
           }
         }
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int m = 0; m < M; ++m) acc[i][m] = __builtin_fmaf(sc[i], part[i][m], acc[i][m]);
       }
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[i][m] = __builtin_fmaf(sc[i], part[i][m], acc[i][m]);
     }
 
     if (it == PPI - 1) {  // tile finished (uniform across the workgroup)
@@ -350,7 +374,13 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
   }
 }
 
-template <int M, int LPR, int R>
+// Measured on the 151936 x 4096 lm_head shape: a grid-stride tile order over a
+// full resident grid beats contiguous per-workgroup ranges and beats an
+// equal-share (smaller) grid.
+constexpr bool kStrided = true;
+constexpr bool kBalanced = false;
+
+template <int M, int LPR, int R, int PB = 1>
 hipError_t launch_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* scales,
                       const uint8_t* zp, void* y, int64_t ldy, int y_type, int N, int K,
                       int block_size, hipStream_t stream) {
@@ -362,9 +392,13 @@ hipError_t launch_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w, const ui
   // x takes 80 bytes of LDS per 32 elements and row.
   const size_t full = (size_t)M * (K / 32) * 80;
   if (full <= (size_t)kLdsBudget) {
-    auto kern = zp ? int4_gemv_persistent<M, LPR, R, true> : int4_gemv_persistent<M, LPR, R, false>;
+    auto kern = zp ? int4_gemv_persistent<M, LPR, R, PB, true, kStrided>
+                   : int4_gemv_persistent<M, LPR, R, PB, false, kStrided>;
     const int cap = resident_workgroups(kern, kBlock, full);
-    const int grid = ntiles < cap ? ntiles : cap;
+    // Equal tile counts per workgroup: the fewest rounds that fit, then the
+    // smallest grid that still covers every tile in that many rounds.
+    const int rounds = (ntiles + cap - 1) / cap;
+    const int grid = kBalanced ? (ntiles + rounds - 1) / rounds : (ntiles < cap ? ntiles : cap);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), full, stream, x, ldx, w, scales, zp, zrow,
                        y, ldy, y_type, N, K, bs_log2, ntiles, x_vec16);
     return hipGetLastError();

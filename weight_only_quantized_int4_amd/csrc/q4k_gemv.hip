@@ -234,7 +234,7 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
 // contiguous share of rows among its wavefronts.  A wavefront owns one row at
 // a time (LPR = 64) and walks a flat sequence of (row, piece) items with a
 // one-item prefetch that crosses row boundaries.
-template <int M, int NT, bool DSC>
+template <int M, int NT, bool DSC, bool STRIDED>
 __global__ __launch_bounds__(NT) void q4k_gemv_persistent(
     const float* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const float2* __restrict__ dsc, float* __restrict__ y, int64_t ldy, int N, int K,
@@ -249,14 +249,19 @@ __global__ __launch_bounds__(NT) void q4k_gemv_persistent(
   const int wv = tid / kWave;
   const int j = tid % kWave;
   const int g = j & 3;
-  const int b = xcd_tile(blockIdx.x, gridDim.x);
-  const int r_begin = (int)((int64_t)b * N / gridDim.x);
-  const int r_end = (int)((int64_t)(b + 1) * N / gridDim.x);
+  // Row order: STRIDED gives wavefront gw rows gw, gw + GW, ... (GW = all
+  // wavefronts of the grid), so the resident wavefronts sweep one compact
+  // window; otherwise a workgroup takes a contiguous range of rows.
+  const int b = STRIDED ? (int)blockIdx.x : xcd_tile(blockIdx.x, gridDim.x);
+  const int r_begin = STRIDED ? 0 : (int)((int64_t)b * N / gridDim.x);
+  const int r_end = STRIDED ? N : (int)((int64_t)(b + 1) * N / gridDim.x);
+  const int first = STRIDED ? b * NW + wv : r_begin + wv;
+  const int rstep = STRIDED ? (int)gridDim.x * NW : NW;
   const int nsb = K >> 8;
   const int P = K >> 6;                  // pieces per row
   const int PPI = (P + kWave - 1) / kWave;  // pieces per lane per row
-  const int span = r_end - r_begin - wv;
-  const int nrows = span > 0 ? (span + NW - 1) / NW : 0;  // rows of this wavefront
+  const int span = r_end - first;
+  const int nrows = span > 0 ? (span + rstep - 1) / rstep : 0;  // rows of this wavefront
   const int nitems = nrows * PPI;
 
   const uint32_t magic = vreg_const(0x64006400u);
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(NT) void q4k_gemv_persistent(
   };
 
   Q4kPiece cur;
-  if (nitems > 0) load(cur, r_begin + wv, 0);
+  if (nitems > 0) load(cur, first, 0);
 
   // Stage x; the chunk sums come out of the same pass when x is 16-byte
   // aligned (8 consecutive lanes hold one 32-element chunk).
@@ -316,13 +321,13 @@ __global__ __launch_bounds__(NT) void q4k_gemv_persistent(
   float acc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.f;
-  int row = r_begin + wv, it = 0;
+  int row = first, it = 0;
 #pragma unroll 1
   for (int u = 0; u < nitems; ++u) {
     int nrow = row, nit = it + 1;
     if (nit == PPI) {
       nit = 0;
-      nrow += NW;
+      nrow += rstep;
     }
     Q4kPiece nxt;
     const bool more = u + 1 < nitems;
@@ -432,6 +437,8 @@ __global__ __launch_bounds__(kBlock) void q4k_plane_kernel(const uint8_t* __rest
   }
 }
 
+constexpr bool kQ4kStrided = false;
+
 template <int M, int LPR, int NT>
 hipError_t launch_cfg(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
                       int64_t ldy, int N, int K, hipStream_t stream) {
@@ -440,7 +447,8 @@ hipError_t launch_cfg(const float* x, int64_t ldx, const uint8_t* w, const float
   // x (68 floats per 64 elements) plus its chunk sums (2 floats per 64), fp32.
   const size_t full = (size_t)M * ((K / 64) * 68 + K / 32) * 4;
   if (full <= (size_t)kLdsBudget) {
-    auto kern = dsc ? q4k_gemv_persistent<M, NT, true> : q4k_gemv_persistent<M, NT, false>;
+    auto kern = dsc ? q4k_gemv_persistent<M, NT, true, kQ4kStrided>
+                    : q4k_gemv_persistent<M, NT, false, kQ4kStrided>;
     const int cap = resident_workgroups(kern, NT, full);
     const int rows_per_wg = NT / kWave;
     const int want = (N + rows_per_wg - 1) / rows_per_wg;
