@@ -90,7 +90,7 @@ def test_strided_and_unaligned_x_and_strided_y():
 
 
 def test_multi_chunk_k():
-    # M = 8 puts at most 3264 elements of x in LDS per pass: K = 8192 takes 3 passes
+    # M = 8 puts at most 3200 elements of x in LDS per pass: K = 8192 takes 3 passes
     N, K = 512, 8192
     say(f"int4 multi-chunk N={N} K={K} M=8")
     p = int4_case(N, K, 32, True, 77)

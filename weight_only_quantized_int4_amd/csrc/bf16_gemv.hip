@@ -90,13 +90,18 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
     }
   }
 
+  __shared__ float red[(kBlock / kWave) * R * M];
+  float tot[R * M];
 #pragma unroll
   for (int i = 0; i < R; ++i)
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float v = group_sum<LPR>(acc[i][m]);
-      if (j == 0 && rows[i] < N) store_out(y, m * ldy + rows[i], v, y_type);
-    }
+    for (int m = 0; m < M; ++m) tot[i * M + m] = acc[i][m];
+  group_sum_wide<LPR, R * M>(tot, red);
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if (j == 0 && rows[i] < N) store_out(y, m * ldy + rows[i], tot[i * M + m], y_type);
 }
 
 template <int M, int LPR>
@@ -167,11 +172,37 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_general(
     }
   }
 
+  __shared__ float red[(kBlock / kWave) * M];
+  group_sum_wide<LPR, M>(acc, red);
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const float v = group_sum<LPR>(acc[m]);
-    if (j == 0 && live) store_out(y, m * ldy + n, v, y_type);
-  }
+  for (int m = 0; m < M; ++m)
+    if (j == 0 && live) store_out(y, m * ldy + n, acc[m], y_type);
+}
+
+template <int M, int LPR, int R>
+hipError_t launch_aligned(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
+                          int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
+  constexpr int RT = (kBlock / LPR) * R;
+  const int grid = (N + RT - 1) / RT;
+  int KC = (kLdsXBudget / (2 * M)) & ~7;
+  if (KC > K) KC = K;
+  const size_t shmem = (size_t)M * KC * 2;
+  hipLaunchKernelGGL((bf16_gemv_aligned<M, LPR, R>), dim3(grid), dim3(kBlock), shmem, stream, x,
+                     ldx, w, ldw, y, ldy, y_type, N, K, KC);
+  return hipGetLastError();
+}
+
+template <int M, int LPR>
+hipError_t launch_general(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
+                          int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
+  constexpr int S = kBlock / LPR;
+  const int grid = (N + S - 1) / S;
+  int KC = (kLdsXBudget / (4 * M) - 8) & ~7;
+  if (KC > K) KC = K;
+  const size_t shmem = (size_t)M * (KC + 8) * 4;
+  hipLaunchKernelGGL((bf16_gemv_general<M, LPR>), dim3(grid), dim3(kBlock), shmem, stream, x, ldx,
+                     w, ldw, y, ldy, y_type, N, K, KC);
+  return hipGetLastError();
 }
 
 template <int M>
@@ -180,27 +211,25 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t l
   const bool aligned = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0) &&
                        ((reinterpret_cast<uintptr_t>(w) & 15) == 0) && (ldw % 8 == 0) &&
                        (K % 8 == 0);
+  // 16 lanes per row, widened for short matrices (see widen_lanes_per_row).
+  const int lpr = widen_lanes_per_row(16, N, (K + 7) / 8);
+  constexpr int R = (M <= 4) ? 2 : 1;
   if (aligned) {
-    constexpr int LPR = 16;
-    constexpr int R = (M <= 4) ? 2 : 1;
-    constexpr int RT = (kBlock / LPR) * R;
-    const int grid = (N + RT - 1) / RT;
-    int KC = (kLdsBudget / (2 * M)) & ~7;
-    if (KC > K) KC = K;
-    const size_t shmem = (size_t)M * KC * 2;
-    hipLaunchKernelGGL((bf16_gemv_aligned<M, LPR, R>), dim3(grid), dim3(kBlock), shmem, stream,
-                       x, ldx, w, ldw, y, ldy, y_type, N, K, KC);
-  } else {
-    constexpr int LPR = 16;
-    constexpr int S = kBlock / LPR;
-    const int grid = (N + S - 1) / S;
-    int KC = (kLdsBudget / (4 * M) - 8) & ~7;
-    if (KC > K) KC = K;
-    const size_t shmem = (size_t)M * (KC + 8) * 4;
-    hipLaunchKernelGGL((bf16_gemv_general<M, LPR>), dim3(grid), dim3(kBlock), shmem, stream, x,
-                       ldx, w, ldw, y, ldy, y_type, N, K, KC);
+    switch (lpr) {
+      case 16: return launch_aligned<M, 16, R>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+      case 32: return launch_aligned<M, 32, R>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+      case 64: return launch_aligned<M, 64, 1>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+      case 128: return launch_aligned<M, 128, 1>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+      default: return launch_aligned<M, 256, 1>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+    }
   }
-  return hipGetLastError();
+  switch (lpr) {
+    case 16: return launch_general<M, 16>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+    case 32: return launch_general<M, 32>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+    case 64: return launch_general<M, 64>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+    case 128: return launch_general<M, 128>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+    default: return launch_general<M, 256>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+  }
 }
 
 }  // namespace

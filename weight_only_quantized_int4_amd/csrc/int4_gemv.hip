@@ -199,13 +199,18 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_kernel(
     }
   }
 
+  __shared__ float red[(kBlock / kWave) * R * M];
+  float tot[R * M];
 #pragma unroll
   for (int i = 0; i < R; ++i)
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float v = group_sum<LPR>(acc[i][m]);
-      if (j == 0 && rows[i] < N) store_out(y, m * ldy + rows[i], v, y_type);
-    }
+    for (int m = 0; m < M; ++m) tot[i * M + m] = acc[i][m];
+  group_sum_wide<LPR, R * M>(tot, red);
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if (j == 0 && rows[i] < N) store_out(y, m * ldy + rows[i], tot[i * M + m], y_type);
 }
 
 // Persistent variant, used whenever all of x fits in LDS: one resident round
@@ -391,7 +396,8 @@ hipError_t launch_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w, const ui
   const int ntiles = (N + RT - 1) / RT;
   // x takes 80 bytes of LDS per 32 elements and row.
   const size_t full = (size_t)M * (K / 32) * 80;
-  if (full <= (size_t)kLdsBudget) {
+  if constexpr (LPR <= kWave) {
+   if (full <= (size_t)kLdsBudget) {
     auto kern = zp ? int4_gemv_persistent<M, LPR, R, PB, true, kStrided>
                    : int4_gemv_persistent<M, LPR, R, PB, false, kStrided>;
     const int cap = resident_workgroups(kern, kBlock, full);
@@ -402,9 +408,10 @@ hipError_t launch_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w, const ui
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), full, stream, x, ldx, w, scales, zp, zrow,
                        y, ldy, y_type, N, K, bs_log2, ntiles, x_vec16);
     return hipGetLastError();
+   }
   }
   const int grid = ntiles;
-  int KC = (kLdsBudget / (80 * M)) * 32;
+  int KC = (kLdsXBudget / (80 * M)) * 32;
   if (KC > K) KC = K;
   const size_t shmem = (size_t)M * (KC / 32) * 80;
   if (zp)
@@ -425,7 +432,7 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
   // Lanes per row (measured on the 151936 x 4096 lm_head shape): 32 is best at
   // small M, 8 at large M (more rows share each x read).  Take the first
   // preference that divides the row's piece count, so no lane idles in the
-  // last stride of a row.
+  // last stride of a row; then widen it for short matrices.
   const int P = K / 32;  // 16-byte pieces per row
   constexpr int pref[3] = {M <= 2 ? 32 : 8, 16, M <= 2 ? 8 : 32};
   int lpr = pref[0];
@@ -434,11 +441,18 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
       lpr = c;
       break;
     }
-  if (lpr == 32)
-    return launch_cfg<M, 32, 2>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
-  if (lpr == 16)
-    return launch_cfg<M, 16, 2>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
-  return launch_cfg<M, 8, 2>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+  lpr = widen_lanes_per_row(lpr, N, P);
+#define QG_LAUNCH(L, RR) \
+  return launch_cfg<M, L, RR>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream)
+  switch (lpr) {
+    case 8: QG_LAUNCH(8, 2);
+    case 16: QG_LAUNCH(16, 2);
+    case 32: QG_LAUNCH(32, 2);
+    case 64: QG_LAUNCH(64, 1);
+    case 128: QG_LAUNCH(128, 1);
+    default: QG_LAUNCH(256, 1);
+  }
+#undef QG_LAUNCH
 }
 
 }  // namespace

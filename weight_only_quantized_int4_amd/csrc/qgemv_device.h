@@ -75,6 +75,37 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Sums NV values per thread over aligned groups of G consecutive threads of a
+// kBlock-thread workgroup.  G <= 64: cross-lane DPP/shuffles, every lane of a
+// group gets the totals.  G = 128 or 256 (a row spread over 2 or 4
+// wavefronts): wavefront totals meet in `red` (LDS, kBlock/64 * NV floats);
+// only the first thread of each group gets the totals.  Every thread of the
+// workgroup must call it (it contains barriers when G > 64).
+template <int G, int NV>
+__device__ __forceinline__ void group_sum_wide(float (&v)[NV], float* red) {
+  if constexpr (G <= kWave) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = group_sum<G>(v[i]);
+  } else {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = group_sum<kWave>(v[i]);
+    __syncthreads();  // red may still be read from a previous call
+    if (lane == 0)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) red[wave * NV + i] = v[i];
+    __syncthreads();
+    if (threadIdx.x % G == 0)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        float t = 0.f;
+#pragma unroll
+        for (int k = 0; k < G / kWave; ++k) t += red[(wave + k) * NV + i];
+        v[i] = t;
+      }
+  }
+}
+
 // Round-to-nearest-even store of an fp32 result in the output type.
 // y_type: 0 = fp16, 1 = bf16, 2 = fp32 (the qg_dtype values).
 __device__ __forceinline__ void store_out(void* y, int64_t idx, float v, int y_type) {

@@ -28,6 +28,20 @@ hipError_t launch_bf16_gemv(const uint16_t* x, int64_t ldx, const uint16_t* w,
 
 // LDS budget per workgroup for staged activations (bytes).
 constexpr int kLdsBudget = 64 * 1024;
+// The same budget less 1 KB for the static reduction buffers of the tiled
+// kernels (the workgroup total stays within 64 KB).
+constexpr int kLdsXBudget = kLdsBudget - 1024;
+
+// Lanes that keep every CU busy: 256 CUs x 8 wavefronts x 64 lanes.
+constexpr int64_t kLanesToFill = 256LL * 8 * 64;
+
+// Lanes per row: start from `lpr` and double it (up to 256, and not past the
+// row's piece count) until the N rows occupy kLanesToFill lanes, so that
+// short, wide matrices still launch enough wavefronts to hide HBM latency.
+inline int widen_lanes_per_row(int lpr, int N, int pieces) {
+  while ((int64_t)N * lpr < kLanesToFill && lpr < 256 && lpr < pieces) lpr *= 2;
+  return lpr;
+}
 
 // Workgroups of `kernel` that fit on the whole device at once: a host-side
 // occupancy calculation (no GPU work), remembered per (kernel, device, LDS).
