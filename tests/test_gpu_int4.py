@@ -65,7 +65,7 @@ def test_block_sizes_and_output_types(bs, out_dtype):
 
 
 def test_odd_block_count_and_tiny_shapes():
-    for (N, K, bs) in [(1, 32, 32), (3, 96, 32), (17, 160, 32), (5, 384, 128)]:
+    for (N, K, bs) in [(1, 32, 32), (3, 96, 32), (17, 160, 32), (5, 128, 32), (5, 384, 128)]:
         say(f"int4 tiny N={N} K={K} bs={bs}")
         p = int4_case(N, K, bs, True, N * K)
         for M in (1, 8):
@@ -178,21 +178,78 @@ def test_invariants():
     q.qgemv_int4_blockwise(f16_dev(p.x[:M]), to_dev(p.w[perm]), f16_dev(p.scales[perm]),
                            to_dev(p.zp[perm]), yp, bs)
     assert np.array_equal(y_host(yp), base[:, perm])
-    # row independence: a row of an M = 2 call equals the M = 1 call on that row
-    # bitwise (same lane mapping and summation order); a row of the M = 8 call
-    # (another lanes-per-row choice) agrees to the tolerance
+    # row independence: M >= 2 runs on the matrix cores (v_mfma), M = 1 on
+    # v_dot2; a row of an M = 2 call equals the same row of an M = 3 call
+    # bitwise (same kernel, rows of the MFMA A operand are independent), and
+    # the M = 1 call agrees to the tolerance
     yr, S = int4_ref(N, K, bs, True, 91)
-    y2 = torch.empty((2, N), dtype=torch.float32, device=DEV)
-    q.qgemv_int4_blockwise(f16_dev(p.x[4:6]), to_dev(p.w), f16_dev(p.scales), to_dev(p.zp), y2, bs)
-    y2 = y_host(y2)
-    for m in (4, 5):
-        y1 = torch.empty((1, N), dtype=torch.float32, device=DEV)
-        q.qgemv_int4_blockwise(f16_dev(p.x[m:m + 1]), to_dev(p.w), f16_dev(p.scales),
-                               to_dev(p.zp), y1, bs)
-        y1 = y_host(y1)[0]
-        assert np.array_equal(y1, y2[m - 4])
-        assert_accept(y1[None], base[m][None], S[m][None] + 0 * yr[m][None], "f32", "row m")
-        assert_accept(base[m][None], yr[m][None], S[m][None], "f32", "row m of M=8")
+    outs = {}
+    for MM in (1, 2, 3):
+        yy = torch.empty((MM, N), dtype=torch.float32, device=DEV)
+        q.qgemv_int4_blockwise(f16_dev(p.x[4:4 + MM]), to_dev(p.w), f16_dev(p.scales),
+                               to_dev(p.zp), yy, bs)
+        outs[MM] = y_host(yy)
+    assert np.array_equal(outs[2], outs[3][:2])
+    assert_accept(outs[1], yr[4:5], S[4:5], "f32", "row 4, M=1")
+    assert_accept(outs[3], yr[4:7], S[4:7], "f32", "rows 4..6, M=3")
+    assert_accept(base, yr[:M], S[:M], "f32", "M=8")
+
+
+# (K, block): K >= 1024 splits each 16-row tile over a workgroup's waves, K <
+# 1024 gives each wave whole tiles; blocks 32 / 64 / >= 128 take the three
+# scale layouts of the matrix-core kernel.
+@pytest.mark.parametrize("K,bs", [(1024, 32), (1024, 64), (1024, 128), (512, 32), (512, 256)])
+def test_one_hot_probe_matrix_core_path_is_bit_exact(K, bs):
+    """M = 4 (v_mfma path): row r of x is one-hot at k_r; y[r, n] must equal the
+    oracle's dequantized w[n, k_r] bitwise (fp32 out)."""
+    N = 48
+    p = int4_case(N, K, bs, True, 33)
+    wdq = oracle.int4_dequant(p.w, p.scales, p.zp, N, K, bs)
+    wd, sd, zd = to_dev(p.w), f16_dev(p.scales), to_dev(p.zp)
+    ks = list(range(0, K, 3))
+    say(f"int4 mfma one-hot probe K={K} bs={bs}: {len(ks)} positions")
+    for i0 in range(0, len(ks), 4):
+        kk = ks[i0:i0 + 4]
+        M = len(kk)
+        x = torch.zeros((M, K), dtype=torch.float16, device=DEV)
+        for r, k in enumerate(kk):
+            x[r, k] = 1.0
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        q.qgemv_int4_blockwise(x, wd, sd, zd, y, bs)
+        got = y.cpu().numpy()
+        want = wdq[:, kk].T.astype(np.float32)
+        assert np.array_equal(got, want), kk
+        nz = want != 0
+        assert np.array_equal(got.view(np.uint32)[nz], want.view(np.uint32)[nz]), kk
+
+
+@pytest.mark.parametrize("bs,asym,M", [(64, True, 4), (128, False, 5), (256, True, 8), (32, True, 2)])
+def test_wide_matrix_sampled(bs, asym, M):
+    # 65576 rows = 4099 tiles of 16: enough for every wave to own whole tiles
+    N, K = 65576, 1024
+    say(f"int4 wide N={N} K={K} bs={bs} asym={asym} M={M}")
+    p = int4_case(N, K, bs, asym, 600 + bs)
+    y = y_host(_run(p, M, torch.float32))
+    rng = np.random.default_rng(3)
+    cols = tuple(sorted(set(rng.integers(0, N, 500).tolist()) | {0, 15, 16, N - 1}))
+    yr, S = int4_ref(N, K, bs, asym, 600 + bs, cols)
+    assert_accept(y[:, list(cols)], yr[:M], S[:M], "f32", f"int4 wide bs={bs} M={M}")
+
+
+def test_misaligned_scales_and_zero_points():
+    # scales 2 bytes past an 8-byte boundary and zero points at an odd address
+    N, K, bs, M = 300, 1024, 32, 4
+    say("int4 misaligned scales / zero points")
+    p = int4_case(N, K, bs, True, 57)
+    nb, zrow = K // bs, p.zp.shape[1]
+    sbuf = f16_dev(np.concatenate([np.zeros(1, np.uint16), p.scales.reshape(-1)]))
+    zbuf = to_dev(np.concatenate([np.zeros(1, np.uint8), p.zp.reshape(-1)]))
+    sd, zd = sbuf[1:].view(N, nb), zbuf[1:].view(N, zrow)
+    assert sd.data_ptr() % 8 == 2 and zd.data_ptr() % 2 == 1
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.qgemv_int4_blockwise(f16_dev(p.x[:M]), to_dev(p.w), sd, zd, y, bs)
+    yr, S = int4_ref(N, K, bs, True, 57)
+    assert_accept(y_host(y), yr[:M], S[:M], "f32", "int4 misaligned scales")
 
 
 def test_empty_and_rejected_calls_on_device():

@@ -31,6 +31,8 @@
 //  * Reduction: the LPR lanes of a row reduce with cross-lane shuffles; no
 //    atomics and no cross-workgroup split-K (the AstrAI commit list measured
 //    split-K as a regression).
+#include <type_traits>
+
 #include "qgemv_device.h"
 #include "qgemv_launch.h"
 
@@ -379,6 +381,283 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
   }
 }
 
+// Matrix-core variant for M >= 2 (where the v_dot2 path turns VALU-bound):
+// v_mfma_f32_16x16x32_f16 with x as the A operand and 16 weight rows as the B
+// operand, so one MFMA contracts 32 k for 16 rows.  A rows M..15 repeat real
+// rows (their D rows are never stored), so every A read is unconditional.
+// Work is cut into items: 4 consecutive 32-weight pieces (128 weights) of a
+// 16-row tile; lane l (n = l % 16, g = l / 16) holds 16 bytes = piece 4c+g of
+// row n of item c.  (q - zp) enters the MFMA exactly as fp16, as in the
+// v_dot2 path, and the fp32 MFMA result is scaled once per scale block (the
+// fp16 scale is exact in fp32).
+//  * PPB (pieces per scale block) = 4 (block >= 128): the item shares one
+//    scale and zero point, so its 4 MFMAs chain their accumulator and need
+//    no data exchange: MFMA t pairs k-group g with word t of every lane's own
+//    16 bytes, i.e. k = (4c+g)*32 + 8t + e.
+//  * PPB = 1 or 2: a 4x4 transpose across the lane groups (two
+//    v_permlane32_swap, two v_permlane16_swap) leaves lane (n, g) holding
+//    8-weight group g of pieces 4c..4c+3, so MFMA t covers exactly piece 4c+t.
+// Memory: items travel in groups of 4.  Per group a lane issues its 4 weight
+// loads back to back (256 contiguous bytes per row across the row's lanes)
+// and one load each of the scales and zero points of item g of the group;
+// three swaps then give every lane those of all 4 items.  (Per-item scale
+// loads touch 16 rows for a few bytes each and cost more than the weights.)
+// DG groups are in flight per lane (a register ring; each slot is refilled as
+// soon as it is consumed, unconditionally: past the last item the row and item
+// indices are clamped, so surplus loads re-read cached bytes).
+// x is staged once per workgroup in LDS in natural order (16-byte slots of 8
+// halves, pre-permuted like the nibble pairs); each row's slots are XOR-
+// swizzled by (row & 3) on the slot bits that the 4 lanes of a row vary, so
+// the A reads of rows 0..3 fall in distinct banks.  SPLIT: all NW waves of a
+// workgroup share one tile and split its items; the partial sums are added in
+// LDS in wave order (deterministic).  Otherwise each wave owns whole tiles.
+// D needs no cross-lane reduction: lane (n, g) ends with rows 4g..4g+3 of
+// column n.
+template <int M, bool ZP, int PPB, bool SPLIT, int NW, int DG>
+__global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zp, int zrow,
+    void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int bs_log2, int ntiles,
+    int x_vec16) {
+  static_assert(PPB == 1 || PPB == 2 || PPB == 4, "pieces per scale block");
+  extern __shared__ uint4 xs[];  // [M][K/8] slots, swizzled; then the SPLIT partials
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n = lane & 15, g = lane >> 4;
+  const int S8 = K >> 3;  // 16-byte slots per x row
+  const int nb = K >> bs_log2;
+  const int C = K >> 7;   // items per row
+  // This wave's stream of tiles (t0, t0 + TS, ...) and its item range per tile.
+  const int t0 = SPLIT ? (int)blockIdx.x : (int)blockIdx.x * NW + wave;
+  const int TS = SPLIT ? (int)gridDim.x : (int)gridDim.x * NW;
+  const int cb = SPLIT ? wave * C / NW : 0;
+  const int ce = SPLIT ? (wave + 1) * C / NW : C;
+  const int my_tiles = t0 < ntiles ? (ntiles - t0 + TS - 1) / TS : 0;
+  const int ngroups = my_tiles * ((ce - cb + 3) >> 2);
+  const uint32_t magic = vreg_const(0x64006400u);
+  // Slot swizzle of x row n: PPB = 4 reads slots 16c + 4g + t, the others
+  // 16c + 4t + g; the swizzle flips the bits that t selects.
+  constexpr int kSwzShift = PPB == 4 ? 0 : 2;
+
+  // Scale bytes of one item: 8 (PPB 1: four blocks), 4 (two) or 2 (one).
+  using SType = std::conditional_t<PPB == 1, uint2, uint32_t>;
+  struct Group {
+    uint4 w[4];  // item j: piece 4(gc+j)+g of row n
+    SType s;     // scales of item gc+g
+    uint32_t z;  // zero-point bytes of item gc+g (PPB 1: 2 bytes, else 1)
+  };
+  const char* sbytes = reinterpret_cast<const char*>(scales);
+  auto issue = [&](Group& gr, int tile, int gc) {
+    const int row = tile * 16 + n;
+    const uint32_t nl = (uint32_t)(row < N ? row : N - 1);
+    const uint32_t wrow = nl * (uint32_t)(K >> 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = gc + j < ce ? gc + j : ce - 1;
+      gr.w[j] = load16(w + (wrow + (uint32_t)(4 * c + g) * 16u));
+    }
+    const int cg = gc + g < ce ? gc + g : ce - 1;
+    const uint32_t blk0 = (uint32_t)((cg << 7) >> bs_log2);  // first block of item cg
+    const char* sp = sbytes + (nl * (uint32_t)nb + blk0) * 2u;
+    if constexpr (PPB == 1) gr.s = *reinterpret_cast<const uint2*>(sp);
+    else if constexpr (PPB == 2) gr.s = *reinterpret_cast<const uint32_t*>(sp);
+    else gr.s = *reinterpret_cast<const uint16_t*>(sp);
+    if constexpr (ZP) {
+      const uint8_t* zq = zp + (nl * (uint32_t)zrow + (blk0 >> 1));
+      gr.z = PPB == 1 ? (uint32_t)*reinterpret_cast<const uint16_t*>(zq) : (uint32_t)*zq;
+    } else {
+      gr.z = 0x8888u;
+    }
+  };
+  auto advance = [&](int& tile, int& gc) {
+    gc += 4;
+    if (gc >= ce) {
+      gc = cb;
+      tile += TS;
+    }
+  };
+
+  Group ring[DG];
+  int lt = t0, lgc = cb;  // next group to load
+  if (ngroups > 0) {
+#pragma unroll
+    for (int k = 0; k < DG; ++k) {
+      issue(ring[k], lt, lgc);
+      advance(lt, lgc);
+    }
+  }
+
+  for (int t = tid; t < M * S8; t += NW * kWave) {
+    const int m = t / S8;
+    const int gi = t - m * S8;
+    const uint16_t* src = x + m * ldx + gi * 8;
+    uint32_t h[8];
+    if (x_vec16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      h[0] = v.x & 0xFFFFu; h[1] = v.x >> 16; h[2] = v.y & 0xFFFFu; h[3] = v.y >> 16;
+      h[4] = v.z & 0xFFFFu; h[5] = v.z >> 16; h[6] = v.w & 0xFFFFu; h[7] = v.w >> 16;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = src[e];
+    }
+    xs[m * S8 + (gi ^ ((m & 3) << kSwzShift))] =
+        make_uint4(h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16),
+                   h[3] | (h[7] << 16));
+  }
+  __syncthreads();
+
+  // LDS byte address of the A slot that MFMA t of item 0 reads (rows >= M
+  // read row n % M).
+  uint32_t aoff[4];
+  const int arow = n < M ? n : n % M;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int slot = PPB == 4 ? 4 * g + t : 4 * t + g;
+    aoff[t] = (uint32_t)((arow * S8 + (slot ^ ((arow & 3) << kSwzShift))) * 16);
+  }
+  const char* xs_bytes = reinterpret_cast<const char*>(xs);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // out[j] = v of lane (n, j): the 32-lane swap pairs lane groups (0,2) and
+  // (1,3), the 16-lane swaps then pair neighbouring groups.
+  auto gather4 = [](uint32_t v, uint32_t (&out)[4]) {
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // v(g&1), v(g&1 | 2)
+    const auto e01 = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+    const auto e23 = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+    out[0] = e01[0]; out[1] = e01[1]; out[2] = e23[0]; out[3] = e23[1];
+  };
+
+  auto consume = [&](const Group& gr, int tile, int gc) {
+    // Scales and zero points of items gc..gc+3, in every lane.
+    uint32_t s_lo[4], s_hi[4], zb[4];
+    if constexpr (PPB == 1) {
+      gather4(gr.s.x, s_lo);
+      gather4(gr.s.y, s_hi);
+    } else {
+      gather4(gr.s, s_lo);
+    }
+    if constexpr (ZP) gather4(gr.z, zb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = gc + j;
+      if (c >= ce) break;  // partial last group of a tile (uniform)
+      const uint32_t ibase = (uint32_t)c * 256u;
+      uint4 av[4];  // A operands of the item's 4 MFMAs
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        av[t] = *reinterpret_cast<const uint4*>(xs_bytes + (aoff[t] + ibase));
+      uint32_t words[4];
+      if constexpr (PPB == 4) {
+        words[0] = gr.w[j].x; words[1] = gr.w[j].y; words[2] = gr.w[j].z; words[3] = gr.w[j].w;
+      } else {
+        // The swaps overwrite their operands: copy the ring slot out first so
+        // that its registers stay free for the refill load.
+        uint32_t d0 = vreg_copy(gr.w[j].x), d1 = vreg_copy(gr.w[j].y),
+                 d2 = vreg_copy(gr.w[j].z), d3 = vreg_copy(gr.w[j].w);
+        // 4x4 transpose (lane group g <-> register t): afterwards word t
+        // holds 8-weight group g of piece 4c+t.
+        const auto r02 = __builtin_amdgcn_permlane32_swap(d0, d2, false, false);
+        const auto r13 = __builtin_amdgcn_permlane32_swap(d1, d3, false, false);
+        d0 = r02[0]; d2 = r02[1]; d1 = r13[0]; d3 = r13[1];
+        const auto r01 = __builtin_amdgcn_permlane16_swap(d0, d1, false, false);
+        const auto r23 = __builtin_amdgcn_permlane16_swap(d2, d3, false, false);
+        words[0] = r01[0]; words[1] = r01[1]; words[2] = r23[0]; words[3] = r23[1];
+      }
+      // Zero-point nibble and fp16 scale bits of block b of item c.
+      auto zero_point = [&](int b) -> uint32_t {
+        if constexpr (!ZP) {
+          return 8u;
+        } else if constexpr (PPB == 4) {
+          const uint32_t blk0 = (uint32_t)((c << 7) >> bs_log2);
+          return (zb[j] >> ((blk0 & 1u) << 2)) & 15u;
+        } else {
+          return (zb[j] >> (4 * b)) & 15u;
+        }
+      };
+      auto scale_bits = [&](int b) -> uint32_t {
+        if constexpr (PPB == 1) return ((b < 2 ? s_lo[j] : s_hi[j]) >> (16 * (b & 1))) & 0xFFFFu;
+        else if constexpr (PPB == 2) return (s_lo[j] >> (16 * b)) & 0xFFFFu;
+        else return s_lo[j] & 0xFFFFu;
+      };
+      f32x4 d = zero4;
+      uint32_t bias_lo = 0, bias_hi = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t % PPB == 0) {
+          const uint32_t z = zero_point(t / PPB);
+          bias_lo = 0xE400E400u + z * 0x00010001u;
+          bias_hi = 0xD400D400u + z * 0x00100010u;
+        }
+        const Pairs8 q = unpack8(words[t], magic, bias_lo, bias_hi);
+        const f16x8 b = {q.a.x, q.a.y, q.b.x, q.b.y, q.c.x, q.c.y, q.d.x, q.d.y};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8>(av[t]), b,
+                                                   t % PPB == 0 ? zero4 : d, 0, 0, 0);
+        if (t % PPB == PPB - 1) {
+          const float sc = f16_to_f32(scale_bits(t / PPB));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, d[i], acc[i]);
+        }
+      }
+      if (c == ce - 1) {  // tile finished: lane (n, g) holds rows 4g..4g+3 of column n
+        const int row = tile * 16 + n;
+        if constexpr (SPLIT) {
+          f32x4* red = reinterpret_cast<f32x4*>(xs + M * S8);  // [NW][64]
+          red[wave * kWave + lane] = acc;
+          __syncthreads();
+          if (wave == 0) {
+            f32x4 sum = red[lane];
+#pragma unroll
+            for (int v = 1; v < NW; ++v) {
+              const f32x4 o = red[v * kWave + lane];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sum[i] += o[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = 4 * g + i;
+              if (m < M && row < N) store_out(y, m * ldy + row, sum[i], y_type);
+            }
+          }
+          __syncthreads();
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 4 * g + i;
+            if (m < M && row < N) store_out(y, m * ldy + row, acc[i], y_type);
+          }
+        }
+        acc = zero4;
+      }
+      // Keep the scheduler from hoisting the next item's A reads (and their
+      // 16 registers) above this item.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  int pt = t0, pgc = cb;  // next group to consume
+  int u = 0;
+#pragma unroll 1
+  for (; u + DG <= ngroups; u += DG) {
+#pragma unroll
+    for (int k = 0; k < DG; ++k) {
+      consume(ring[k], pt, pgc);
+      advance(pt, pgc);
+      issue(ring[k], lt, lgc);
+      advance(lt, lgc);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < DG; ++k) {
+    if (u + k < ngroups) {
+      consume(ring[k], pt, pgc);
+      advance(pt, pgc);
+    }
+  }
+}
+
 // Measured on the 151936 x 4096 lm_head shape: a grid-stride tile order over a
 // full resident grid beats contiguous per-workgroup ranges and beats an
 // equal-share (smaller) grid.
@@ -425,10 +704,82 @@ hipError_t launch_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w, const ui
   return hipGetLastError();
 }
 
+// Smallest M that takes the matrix-core kernel.
+constexpr int kMfmaMinM = 2;
+
+// Matrix-core launch shape: waves per workgroup and register groups (of 4
+// items) in flight per lane.
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaDepth = 1;
+
+template <int M, int PPB, bool SPLIT>
+hipError_t launch_mfma_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w,
+                           const uint16_t* scales, const uint8_t* zp, void* y, int64_t ldy,
+                           int y_type, int N, int K, int block_size, size_t shmem, int grid_cap,
+                           hipStream_t stream) {
+  constexpr int NW = kMfmaWaves;
+  const int bs_log2 = __builtin_ctz((unsigned)block_size);
+  const int zrow = ((K / block_size) + 1) / 2;
+  const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
+  const int ntiles = (N + 15) / 16;
+  auto kern = zp ? int4_gemv_mfma<M, true, PPB, SPLIT, NW, kMfmaDepth>
+                 : int4_gemv_mfma<M, false, PPB, SPLIT, NW, kMfmaDepth>;
+  const int cap = resident_workgroups(kern, NW * kWave, shmem);
+  const int want = SPLIT ? ntiles : (ntiles + NW - 1) / NW;
+  int grid = want < cap ? want : cap;
+  if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * kWave), shmem, stream, x, ldx, w, scales, zp,
+                     zrow, y, ldy, y_type, N, K, bs_log2, ntiles, x_vec16);
+  return hipGetLastError();
+}
+
+// Whole tiles per wave when the tiles fill at least half of the resident
+// wavefront slots; otherwise (and when every wave gets at least one item and
+// the partial sums fit in LDS) the waves of a workgroup split each tile.
+template <int M, int PPB>
+hipError_t launch_mfma_ppb(const uint16_t* x, int64_t ldx, const uint8_t* w,
+                           const uint16_t* scales, const uint8_t* zp, void* y, int64_t ldy,
+                           int y_type, int N, int K, int block_size, hipStream_t stream) {
+  constexpr int NW = kMfmaWaves;
+  const size_t xbytes = (size_t)M * K * 2;
+  const size_t split_bytes = xbytes + (size_t)NW * kWave * 16;
+  const int ntiles = (N + 15) / 16;
+  if (K / 128 >= NW && split_bytes <= (size_t)kLdsBudget) {
+    auto whole = int4_gemv_mfma<M, true, PPB, false, NW, kMfmaDepth>;
+    const int64_t waves = (int64_t)resident_workgroups(whole, NW * kWave, xbytes) * NW;
+    if (2LL * ntiles < waves)
+      return launch_mfma_cfg<M, PPB, true>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
+                                           block_size, split_bytes, 0, stream);
+  }
+  return launch_mfma_cfg<M, PPB, false>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size,
+                                        xbytes, 0, stream);
+}
+
+template <int M>
+hipError_t launch_mfma(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* scales,
+                       const uint8_t* zp, void* y, int64_t ldy, int y_type, int N, int K,
+                       int block_size, hipStream_t stream) {
+  if (block_size >= 128)
+    return launch_mfma_ppb<M, 4>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+  if (block_size == 64)
+    return launch_mfma_ppb<M, 2>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+  return launch_mfma_ppb<M, 1>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+}
+
 template <int M>
 hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* scales,
                     const uint8_t* zp, void* y, int64_t ldy, int y_type, int N, int K,
                     int block_size, hipStream_t stream) {
+  if constexpr (M >= kMfmaMinM) {
+    // The matrix-core kernel reads an item's scales with one load of
+    // 8 * 32 / block_size bytes (at least 2) and, for block 32, its zero
+    // points with one 2-byte load: both need matching base alignment.
+    const uintptr_t salign = block_size >= 128 ? 2 : (size_t)8 * 32 / block_size;
+    const bool aligned = (reinterpret_cast<uintptr_t>(scales) % salign == 0) &&
+                         (block_size != 32 || reinterpret_cast<uintptr_t>(zp) % 2 == 0);
+    if (K % 128 == 0 && (size_t)M * K * 2 <= (size_t)kLdsBudget && aligned)
+      return launch_mfma<M>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+  }
   // Lanes per row (measured on the 151936 x 4096 lm_head shape): 32 is best at
   // small M, 8 at large M (more rows share each x read).  Take the first
   // preference that divides the row's piece count, so no lane idles in the

@@ -13,6 +13,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts)
@@ -48,6 +50,14 @@ __device__ __forceinline__ uint32_t vreg_const(uint32_t c) {
   uint32_t v;
   asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(c));
   return v;
+}
+
+// A register-to-register copy the compiler cannot fold away: gives a value a
+// register of its own (for instructions that overwrite their operands).
+__device__ __forceinline__ uint32_t vreg_copy(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
 }
 
 // DPP lane permutes within a row of 16 lanes.
