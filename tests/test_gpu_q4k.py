@@ -83,18 +83,54 @@ def test_m_sweep(M):
     assert np.array_equal(yd, y_host(y2))
 
 
-def test_multi_chunk_k_and_strided_x():
-    # M = 8 stages at most 1792 elements of x per pass: K = 11008 takes 7 passes
+@pytest.mark.parametrize("M", [2, 3])
+def test_long_rows_x_resident(M):
+    # K = 11008: x and its chunk sums take 94 KB (M = 2) and 141 KB (M = 3) of
+    # LDS, so the whole of x stays resident in one workgroup
+    N, K = 700, 11008
+    p = q4k_case(N, K, 422)
+    yr, S = q4k_ref(N, K, 422)
+    xd, wd = to_dev(p.x[:M]), to_dev(p.w)
+    say(f"q4k long rows M={M} N={N} K={K}")
+    y = torch.full((M, N), float("nan"), device=DEV)
+    q.qgemv_q4k(xd, wd, y)
+    yd = y_host(y)
+    assert_accept(yd, yr[:M], S[:M], "f32", f"q4k K={K} M={M}")
+    y2 = torch.full((M, N), float("nan"), device=DEV)
+    q.qgemv_q4k_dsc(xd, wd, _plane(wd, N, K), y2)
+    assert np.array_equal(yd, y_host(y2))
+
+
+def test_row_groups_and_strided_x():
+    # K = 11008, M = 8: x does not fit in LDS, 3 rows do; three row groups
     N, K, M = 300, 11008, 8
     p = q4k_case(N, K, 421)
     yr, S = q4k_ref(N, K, 421)
     buf = np.zeros((M, K + 3), dtype=np.float32)
     buf[:, 1:K + 1] = p.x[:M]
     xt = to_dev(buf)[:, 1:K + 1]  # ldx = K + 3, 4-byte (not 16-byte) aligned
-    say("q4k multi-chunk strided x")
+    say("q4k row groups, strided x")
     y = torch.full((M, N + 2), float("nan"), device=DEV)[:, :N]
     q.qgemv_q4k(xt, to_dev(p.w), y)
-    assert_accept(y_host(y), yr, S, "f32", "q4k multi-chunk")
+    assert_accept(y_host(y), yr, S, "f32", "q4k row groups")
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_multi_chunk_k(M):
+    # K = 40960: one row of x and its chunk sums exceed 160 KB, so x is staged
+    # in LDS one K chunk (a whole number of super-blocks) at a time
+    N, K = 64, 40960
+    p = q4k_case(N, K, 423)
+    yr, S = q4k_ref(N, K, 423)
+    xd, wd = to_dev(p.x[:M]), to_dev(p.w)
+    say(f"q4k multi-chunk K={K} M={M}")
+    y = torch.full((M, N), float("nan"), device=DEV)
+    q.qgemv_q4k(xd, wd, y)
+    yd = y_host(y)
+    assert_accept(yd, yr[:M], S[:M], "f32", f"q4k multi-chunk M={M}")
+    y2 = torch.full((M, N), float("nan"), device=DEV)
+    q.qgemv_q4k_dsc(xd, wd, _plane(wd, N, K), y2)
+    assert np.array_equal(yd, y_host(y2))
 
 
 def test_one_hot_probe_is_bit_exact():

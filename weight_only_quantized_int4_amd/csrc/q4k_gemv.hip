@@ -233,9 +233,12 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
 // resident round of workgroups; each stages x once and splits an equal,
 // contiguous share of rows among its wavefronts.  A wavefront owns one row at
 // a time (LPR = 64) and walks a flat sequence of (row, piece) items with a
-// one-item prefetch that crosses row boundaries.
-template <int M, int NT, bool DSC, bool STRIDED>
-__global__ __launch_bounds__(NT) void q4k_gemv_persistent(
+// register ring of D items that crosses row boundaries.
+// M = 1 with 1024-thread workgroups asks for 64 VGPRs (8 wavefronts per SIMD),
+// so that two workgroups share a CU.
+template <int M, int NT, bool DSC, bool STRIDED, int D>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(M == 1 && NT == 1024 ? 8 : 1)))
+void q4k_gemv_persistent(
     const float* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const float2* __restrict__ dsc, float* __restrict__ y, int64_t ldy, int N, int K,
     int x_vec16) {
@@ -270,6 +273,7 @@ __global__ __launch_bounds__(NT) void q4k_gemv_persistent(
   const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
 
   auto load = [&](Q4kPiece& st, int row, int it) {
+    row = row < N ? row : N - 1;  // ring refills past this wavefront's last row
     int p = j + kWave * it;
     p = p < P ? p : P - 1;  // idle lanes of a ragged last stride re-read a valid piece
     const uint32_t sb = (uint32_t)(p >> 2);
@@ -284,9 +288,23 @@ __global__ __launch_bounds__(NT) void q4k_gemv_persistent(
       st.h = load16(w + bo);
     }
   };
+  auto advance = [&](int& row, int& it) {
+    it = it + 1 == PPI ? 0 : it + 1;
+    row = it == 0 ? row + rstep : row;
+  };
 
-  Q4kPiece cur;
-  if (nitems > 0) load(cur, first, 0);
+  // D items in flight per lane: a register ring, each slot refilled as soon
+  // as it is consumed (unconditionally; past the last item the row index is
+  // clamped, so surplus loads re-read cached bytes).
+  Q4kPiece ring[D];
+  int lrow = first, lit = 0;  // next item to load
+  if (nitems > 0) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      load(ring[k], lrow, lit);
+      advance(lrow, lit);
+    }
+  }
 
   // Stage x; the chunk sums come out of the same pass when x is 16-byte
   // aligned (8 consecutive lanes hold one 32-element chunk).
@@ -321,18 +339,8 @@ __global__ __launch_bounds__(NT) void q4k_gemv_persistent(
   float acc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.f;
-  int row = first, it = 0;
-#pragma unroll 1
-  for (int u = 0; u < nitems; ++u) {
-    int nrow = row, nit = it + 1;
-    if (nit == PPI) {
-      nit = 0;
-      nrow += rstep;
-    }
-    Q4kPiece nxt;
-    const bool more = u + 1 < nitems;
-    if (more) load(nxt, nrow, nit);
 
+  auto consume = [&](const Q4kPiece& cur, int row, int it) {
     const int p = j + kWave * it;
     if (p < P) {
       float dva, mva, dvb, mvb;
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(NT) void q4k_gemv_persistent(
         const f16x2 C = bitcast<f16x2>((w8 & 0x000F000Fu) | magic) + m1024;
         const f16x2 B = __builtin_elementwise_fma(
             bitcast<f16x2>((word & 0x00F000F0u) | magic), sixteenth, m64);
-        const f16x2 D = __builtin_elementwise_fma(
+        const f16x2 D2 = __builtin_elementwise_fma(
             bitcast<f16x2>((w8 & 0x00F000F0u) | magic), sixteenth, m64);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
@@ -372,9 +380,9 @@ __global__ __launch_bounds__(NT) void q4k_gemv_persistent(
           u0 = __builtin_fmaf((float)A.y, xa4.z, u0);
           u0 = __builtin_fmaf((float)C.y, xa4.w, u0);
           v0 = __builtin_fmaf((float)B.x, xb4.x, v0);
-          v0 = __builtin_fmaf((float)D.x, xb4.y, v0);
+          v0 = __builtin_fmaf((float)D2.x, xb4.y, v0);
           v0 = __builtin_fmaf((float)B.y, xb4.z, v0);
-          v0 = __builtin_fmaf((float)D.y, xb4.w, v0);
+          v0 = __builtin_fmaf((float)D2.y, xb4.w, v0);
           pa[m] = u0;
           pb[m] = v0;
         }
@@ -398,9 +406,26 @@ __global__ __launch_bounds__(NT) void q4k_gemv_persistent(
         if (j == 0) y[m * ldy + row] = v;
       }
     }
-    if (more) cur = nxt;
-    row = nrow;
-    it = nit;
+  };
+
+  int prow = first, pit = 0;  // next item to consume
+  int u = 0;
+#pragma unroll 1
+  for (; u + D <= nitems; u += D) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      consume(ring[k], prow, pit);
+      advance(prow, pit);
+      load(ring[k], lrow, lit);
+      advance(lrow, lit);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    if (u + k < nitems) {
+      consume(ring[k], prow, pit);
+      advance(prow, pit);
+    }
   }
 }
 
@@ -438,17 +463,27 @@ __global__ __launch_bounds__(kBlock) void q4k_plane_kernel(const uint8_t* __rest
 }
 
 constexpr bool kQ4kStrided = false;
+// Items (64-weight pieces) in flight per lane in the persistent kernel.
+constexpr int kQ4kDepth = 1;
 
-template <int M, int LPR, int NT>
-hipError_t launch_cfg(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
-                      int64_t ldy, int N, int K, hipStream_t stream) {
+// Persistent kernel (1024 threads: 16 rows in flight per workgroup, x staged
+// once) whenever x and its chunk sums fit in a workgroup's LDS (up to 160 KB);
+// otherwise the K-chunked tiled kernel (256 threads: it keeps the full
+// register file for its M accumulators per row).
+template <int M>
+hipError_t launch_m(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
+                    int64_t ldy, int N, int K, hipStream_t stream) {
+  constexpr int NT = 1024, LPR = 64, NT_TILED = 256;
   const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 4 == 0);
   const float2* dsc2 = reinterpret_cast<const float2*>(dsc);
   // x (68 floats per 64 elements) plus its chunk sums (2 floats per 64), fp32.
   const size_t full = (size_t)M * ((K / 64) * 68 + K / 32) * 4;
-  if (full <= (size_t)kLdsBudget) {
-    auto kern = dsc ? q4k_gemv_persistent<M, NT, true, kQ4kStrided>
-                    : q4k_gemv_persistent<M, NT, false, kQ4kStrided>;
+  if (full <= (size_t)kLdsMax) {
+    constexpr int D = M == 1 ? kQ4kDepth : 1;
+    auto kern = dsc ? q4k_gemv_persistent<M, NT, true, kQ4kStrided, D>
+                    : q4k_gemv_persistent<M, NT, false, kQ4kStrided, D>;
+    const hipError_t e = allow_lds(kern, full);
+    if (e != hipSuccess) return e;
     const int cap = resident_workgroups(kern, NT, full);
     const int rows_per_wg = NT / kWave;
     const int want = (N + rows_per_wg - 1) / rows_per_wg;
@@ -457,36 +492,39 @@ hipError_t launch_cfg(const float* x, int64_t ldx, const uint8_t* w, const float
                        x_vec16);
     return hipGetLastError();
   }
-  constexpr int S = NT / LPR;
+  constexpr int S = NT_TILED / LPR;
   const int grid = (N + S - 1) / S;
   // KC a multiple of 256 (whole super-blocks) within the LDS budget.
   int KC = (kLdsBudget / (4 * 70 * M)) * 64 & ~255;
   if (KC > K) KC = K;
   const size_t shmem = (size_t)M * ((KC / 64) * 68 + KC / 32) * 4;
   if (dsc)
-    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT, true>), dim3(grid), dim3(NT), shmem, stream,
-                       x, ldx, w, dsc2, y, ldy, N, K, KC, x_vec16);
+    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT_TILED, true>), dim3(grid), dim3(NT_TILED),
+                       shmem, stream, x, ldx, w, dsc2, y, ldy, N, K, KC, x_vec16);
   else
-    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT, false>), dim3(grid), dim3(NT), shmem, stream,
-                       x, ldx, w, nullptr, y, ldy, N, K, KC, x_vec16);
+    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT_TILED, false>), dim3(grid), dim3(NT_TILED),
+                       shmem, stream, x, ldx, w, nullptr, y, ldy, N, K, KC, x_vec16);
   return hipGetLastError();
-}
-
-template <int M>
-hipError_t launch_m(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
-                    int64_t ldy, int N, int K, hipStream_t stream) {
-  // 1024-thread workgroups cap a lane at 128 VGPRs: enough for M = 1 only;
-  // larger M keeps 4 rows per workgroup and the full register file.
-  if constexpr (M == 1)
-    return launch_cfg<M, 64, 1024>(x, ldx, w, dsc, y, ldy, N, K, stream);
-  else
-    return launch_cfg<M, 64, 256>(x, ldx, w, dsc, y, ldy, N, K, stream);
 }
 
 }  // namespace
 
 hipError_t launch_q4k_gemv(const float* x, int64_t ldx, const uint8_t* w, const float* dsc,
                            float* y, int64_t ldy, int M, int N, int K, hipStream_t stream) {
+  // When x (all M rows) does not fit in a workgroup's LDS but a few rows do,
+  // run the persistent kernel on groups of rows: each group re-reads the
+  // weights, which beats restaging x for every 4 rows in the tiled kernel.
+  const size_t per_row = ((size_t)(K / 64) * 68 + K / 32) * 4;
+  const int mfit = (int)((size_t)kLdsMax / per_row);
+  if (M > mfit && mfit >= 1) {
+    for (int m0 = 0; m0 < M; m0 += mfit) {
+      const int mm = M - m0 < mfit ? M - m0 : mfit;
+      const hipError_t e = launch_q4k_gemv(x + m0 * ldx, ldx, w, dsc, y + m0 * ldy, ldy, mm, N,
+                                           K, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   switch (M) {
 #define QG_CASE(MM) \
   case MM:          \

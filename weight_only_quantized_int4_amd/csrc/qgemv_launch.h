@@ -28,6 +28,9 @@ hipError_t launch_bf16_gemv(const uint16_t* x, int64_t ldx, const uint16_t* w,
 
 // LDS budget per workgroup for staged activations (bytes).
 constexpr int kLdsBudget = 64 * 1024;
+// gfx950 gives a workgroup up to 160 KB of LDS; a kernel must raise its
+// dynamic-LDS limit (allow_lds) before it is launched with more than 64 KB.
+constexpr int kLdsMax = 160 * 1024;
 // The same budget less 1 KB for the static reduction buffers of the tiled
 // kernels (the workgroup total stays within 64 KB).
 constexpr int kLdsXBudget = kLdsBudget - 1024;
@@ -80,5 +83,29 @@ inline int resident_workgroups(F kernel, int threads, size_t shmem) {
   return value;
 }
 
+// Raise `kernel`'s dynamic-LDS limit to `bytes` when that is above 64 KB
+// (once per kernel, device and size).
+template <typename F>
+inline hipError_t allow_lds(F kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  struct Entry {
+    const void* fn;
+    int dev;
+    size_t bytes;
+  };
+  static std::mutex mu;
+  static Entry table[256];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (table[i].fn == fn && table[i].dev == dev && table[i].bytes >= bytes) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && used < 256) table[used++] = Entry{fn, dev, bytes};
+  return e;
+}
 
 }  // namespace qg
