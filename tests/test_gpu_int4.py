@@ -90,13 +90,28 @@ def test_strided_and_unaligned_x_and_strided_y():
 
 
 def test_multi_chunk_k():
-    # M = 8 puts at most 3200 elements of x in LDS per pass: K = 8192 takes 3 passes
-    N, K = 512, 8192
+    # K = 8224 (not a multiple of 128: v_dot2 kernel); M = 8 puts at most 3200
+    # elements of x in LDS per pass, so K takes 3 passes
+    N, K = 512, 8224
     say(f"int4 multi-chunk N={N} K={K} M=8")
     p = int4_case(N, K, 32, True, 77)
     y = y_host(_run(p, 8, torch.float32))
     yr, S = int4_ref(N, K, 32, True, 77)
     assert_accept(y, yr, S, "f32", "int4 multi-chunk")
+
+
+@pytest.mark.parametrize("N", [512, 40000])
+def test_matrix_core_x_above_64k(N):
+    # M = 8, K = 8192: x takes 128 KB of LDS (one workgroup per CU); N = 512
+    # splits tiles over the waves of a workgroup, N = 40000 gives whole tiles
+    K, M = 8192, 8
+    say(f"int4 matrix-core large x N={N} K={K} M={M}")
+    p = int4_case(N, K, 32, True, 78)
+    y = y_host(_run(p, M, torch.float32))
+    cols = None if N == 512 else tuple(sorted(set(np.random.default_rng(4).integers(0, N, 400).tolist()) | {N - 1}))
+    yr, S = int4_ref(N, K, 32, True, 78, cols)
+    got = y if cols is None else y[:, list(cols)]
+    assert_accept(got, yr[:M], S[:M], "f32", f"int4 large x N={N}")
 
 
 @pytest.mark.parametrize("M", [1, 8])

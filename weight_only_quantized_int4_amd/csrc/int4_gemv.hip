@@ -715,7 +715,7 @@ constexpr int kMfmaDepth = 1;
 template <int M, int PPB, bool SPLIT>
 hipError_t launch_mfma_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w,
                            const uint16_t* scales, const uint8_t* zp, void* y, int64_t ldy,
-                           int y_type, int N, int K, int block_size, size_t shmem, int grid_cap,
+                           int y_type, int N, int K, int block_size, size_t shmem,
                            hipStream_t stream) {
   constexpr int NW = kMfmaWaves;
   const int bs_log2 = __builtin_ctz((unsigned)block_size);
@@ -724,10 +724,11 @@ hipError_t launch_mfma_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w,
   const int ntiles = (N + 15) / 16;
   auto kern = zp ? int4_gemv_mfma<M, true, PPB, SPLIT, NW, kMfmaDepth>
                  : int4_gemv_mfma<M, false, PPB, SPLIT, NW, kMfmaDepth>;
+  const hipError_t e = allow_lds(kern, shmem);
+  if (e != hipSuccess) return e;
   const int cap = resident_workgroups(kern, NW * kWave, shmem);
   const int want = SPLIT ? ntiles : (ntiles + NW - 1) / NW;
-  int grid = want < cap ? want : cap;
-  if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
+  const int grid = want < cap ? want : cap;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * kWave), shmem, stream, x, ldx, w, scales, zp,
                      zrow, y, ldy, y_type, N, K, bs_log2, ntiles, x_vec16);
   return hipGetLastError();
@@ -744,15 +745,17 @@ hipError_t launch_mfma_ppb(const uint16_t* x, int64_t ldx, const uint8_t* w,
   const size_t xbytes = (size_t)M * K * 2;
   const size_t split_bytes = xbytes + (size_t)NW * kWave * 16;
   const int ntiles = (N + 15) / 16;
-  if (K / 128 >= NW && split_bytes <= (size_t)kLdsBudget) {
+  if (K / 128 >= NW && split_bytes <= (size_t)kLdsMax) {
     auto whole = int4_gemv_mfma<M, true, PPB, false, NW, kMfmaDepth>;
+    const hipError_t e = allow_lds(whole, xbytes);
+    if (e != hipSuccess) return e;
     const int64_t waves = (int64_t)resident_workgroups(whole, NW * kWave, xbytes) * NW;
     if (2LL * ntiles < waves)
       return launch_mfma_cfg<M, PPB, true>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
-                                           block_size, split_bytes, 0, stream);
+                                           block_size, split_bytes, stream);
   }
   return launch_mfma_cfg<M, PPB, false>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size,
-                                        xbytes, 0, stream);
+                                        xbytes, stream);
 }
 
 template <int M>
@@ -777,7 +780,7 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
     const uintptr_t salign = block_size >= 128 ? 2 : (size_t)8 * 32 / block_size;
     const bool aligned = (reinterpret_cast<uintptr_t>(scales) % salign == 0) &&
                          (block_size != 32 || reinterpret_cast<uintptr_t>(zp) % 2 == 0);
-    if (K % 128 == 0 && (size_t)M * K * 2 <= (size_t)kLdsBudget && aligned)
+    if (K % 128 == 0 && (size_t)M * K * 2 <= (size_t)kLdsMax && aligned)
       return launch_mfma<M>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
   }
   // Lanes per row (measured on the 151936 x 4096 lm_head shape): 32 is best at
