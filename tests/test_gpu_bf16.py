@@ -87,6 +87,45 @@ def test_long_unaligned_k_multi_chunk():
     assert_accept(y_host(y), yr, S, "f32", "bf16 general multi-chunk")
 
 
+@pytest.mark.parametrize("K", [1024, 512])
+def test_one_hot_probe_matrix_core_path_is_bit_exact(K):
+    """M = 4 (v_mfma path; K = 1024 splits each tile over a workgroup's waves,
+    K = 512 gives whole tiles): row r of x is one-hot at k_r, so y[r, n] must
+    equal w[n, k_r] (bf16 -> fp32 is exact) bitwise."""
+    N = 48
+    p = bf16_case(N, K, 350 + K)
+    wd = bf16_dev(p.w)
+    want_all = (p.w.astype(np.uint32) << 16).view(np.float32)
+    ks = list(range(0, K, 3))
+    say(f"bf16 mfma one-hot probe K={K}: {len(ks)} positions")
+    for i0 in range(0, len(ks), 4):
+        kk = ks[i0:i0 + 4]
+        M = len(kk)
+        x = torch.zeros((M, K), dtype=torch.bfloat16, device=DEV)
+        for r, k in enumerate(kk):
+            x[r, k] = 1.0
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        q.gemv_bf16(x, wd, y)
+        got = y.cpu().numpy()
+        want = want_all[:, kk].T
+        assert np.array_equal(got, want), kk
+        nz = want != 0
+        assert np.array_equal(got.view(np.uint32)[nz], want.view(np.uint32)[nz]), kk
+
+
+@pytest.mark.parametrize("M", [2, 5])
+def test_wide_matrix_sampled(M):
+    # 40000 rows = 2500 tiles of 16: every wave owns whole tiles
+    N, K = 40000, 1536
+    p = bf16_case(N, K, 360)
+    say(f"bf16 wide N={N} K={K} M={M}")
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_bf16(bf16_dev(p.x[:M]), bf16_dev(p.w), y)
+    cols = sorted(set(np.random.default_rng(6).integers(0, N, 500).tolist()) | {0, 15, 16, N - 1})
+    yr, S = _ref(p, M, cols=cols)
+    assert_accept(y_host(y)[:, cols], yr, S, "f32", f"bf16 wide M={M}")
+
+
 def test_invariants_and_stream():
     p = bf16_case(1536, 1536, 301)
     xd, wd = bf16_dev(p.x[:4]), bf16_dev(p.w)
@@ -96,10 +135,10 @@ def test_invariants_and_stream():
     base = y_host(y)
     q.gemv_bf16(xd, wd, y)
     assert np.array_equal(base, y_host(y))
-    # v_dot2_f32_bf16 is not sign-symmetric in its rounding on gfx950 (a
-    # probe of the instruction against exact arithmetic shows ~1% of random
-    # cases off round-to-nearest), so y(-x) = -y(x) holds to the tolerance,
-    # not bitwise.
+    # y(-x) = -y(x) is checked to the tolerance, not bitwise: v_dot2_f32_bf16
+    # (M = 1) is not sign-symmetric in its rounding on gfx950 (a probe of the
+    # instruction against exact arithmetic shows ~1% of random cases off
+    # round-to-nearest).
     q.gemv_bf16(-xd, wd, y)
     yr, S = _ref(p, 4)
     assert_accept(-y_host(y), yr, S, "f32", "bf16 y(-x)")

@@ -115,10 +115,11 @@ def test_row_groups_and_strided_x():
     assert_accept(y_host(y), yr, S, "f32", "q4k row groups")
 
 
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 8])
 def test_multi_chunk_k(M):
     # K = 40960: one row of x and its chunk sums exceed 160 KB, so x is staged
-    # in LDS one K chunk (a whole number of super-blocks) at a time
+    # in LDS one K chunk (a whole number of super-blocks) at a time, for at
+    # most 4 rows of x per launch
     N, K = 64, 40960
     p = q4k_case(N, K, 423)
     yr, S = q4k_ref(N, K, 423)

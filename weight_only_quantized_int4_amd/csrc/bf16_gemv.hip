@@ -4,7 +4,7 @@
 // Operation (the bf16 GEMV primitive of the AstrAI backend commit list):
 //     y[m,n] = sum_k x[m,k] * w[n,k]
 //
-// Two kernels, chosen per call on the host:
+// Three kernels, chosen per call on the host:
 //  * aligned: x and W rows 16-byte aligned and K a multiple of 8 (the
 //    production case with allocator-aligned tensors).  Pure 128-bit weight
 //    loads, x staged as bf16 in LDS, v_dot2_f32_bf16 (exact bf16 products,
@@ -16,6 +16,7 @@
 //    8-element halo, and every product is one fp32 FMA.
 // Both keep one row per group of LPR lanes and reduce with cross-lane
 // shuffles; no split-K (measured as a regression on the page).
+//  * matrix core (M >= 2, aligned, K a multiple of 128): see bf16_gemv_mfma.
 #include "qgemv_device.h"
 #include "qgemv_launch.h"
 
@@ -59,10 +60,16 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
     uint4 cur[R];
     if (j < P) load(cur, j);
     __syncthreads();
-    for (int t = tid; t < M * P; t += kBlock) {
-      const int m = t / P, i = t - m * P;
-      xs[m * G + i] = *reinterpret_cast<const uint4*>(x + m * ldx + kc + 8 * i);
-    }
+    stage_slots<4>(
+        tid, kBlock, M * P,
+        [&](int t) {
+          const int m = t / P;
+          return *reinterpret_cast<const uint4*>(x + m * ldx + kc + 8 * (t - m * P));
+        },
+        [&](int t, uint4 v) {
+          const int m = t / P;
+          xs[m * G + (t - m * P)] = v;
+        });
     __syncthreads();
 #pragma unroll 1
     for (int p = j; p < P; p += LPR) {
@@ -179,6 +186,197 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_general(
     if (j == 0 && live) store_out(y, m * ldy + n, acc[m], y_type);
 }
 
+// Matrix-core variant for M >= 2 (16-byte aligned rows, K a multiple of 128):
+// v_mfma_f32_16x16x32_bf16 with x as the A operand (M rows; A rows M..15
+// repeat real rows and their D rows are never stored) and 16 weight rows as
+// the B operand.  An item is 128 k of a 16-row tile; lane (n, g) loads
+// k = 128c + 32t + 8g .. +8 of row n for t = 0..3 (each load instruction
+// reads 64 contiguous bytes of 16 rows), which is exactly the B operand of
+// MFMA t over k = 128c + 32t .. +32.  bf16 products are exact and the 4
+// MFMAs of every item chain into one fp32 accumulator, so the loop carries no
+// vector ALU work beyond LDS addressing.  x is staged once per workgroup in
+// LDS (16-byte slots of 8 elements, XOR-swizzled by 4 * (row & 3) so the A
+// reads of rows 0..3 fall in distinct banks).  Tiles, the D-item register
+// ring and the SPLIT partial sums follow the int4 matrix-core kernel.
+template <int M, bool SPLIT, int NW, int D>
+__global__ __launch_bounds__(NW * kWave) void bf16_gemv_mfma(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw,
+    void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int ntiles, int x_vec16) {
+  extern __shared__ uint4 xs[];  // [M][K/8] slots, swizzled; then the SPLIT partials
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n = lane & 15, g = lane >> 4;
+  const int S8 = K >> 3;
+  const int C = K >> 7;
+  const int t0 = SPLIT ? (int)blockIdx.x : (int)blockIdx.x * NW + wave;
+  const int TS = SPLIT ? (int)gridDim.x : (int)gridDim.x * NW;
+  const int cb = SPLIT ? wave * C / NW : 0;
+  const int ce = SPLIT ? (wave + 1) * C / NW : C;
+  const int my_tiles = t0 < ntiles ? (ntiles - t0 + TS - 1) / TS : 0;
+  const int nitems = my_tiles * (ce - cb);
+
+  struct Item {
+    uint4 w[4];
+  };
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(w);
+  auto issue = [&](Item& it, int tile, int c) {
+    const int row = tile * 16 + n;
+    // byte offset (tensors are below 4 GiB): a 32-bit offset off a uniform
+    // base keeps each load to one address register
+    const uint32_t base =
+        ((uint32_t)(row < N ? row : N - 1) * (uint32_t)ldw + (uint32_t)(128 * c + 8 * g)) * 2u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) it.w[t] = load16(wb + (base + 64u * t));
+  };
+  auto advance = [&](int& tile, int& c) {
+    c = c + 1 == ce ? cb : c + 1;
+    tile = c == cb ? tile + TS : tile;
+  };
+
+  Item ring[D];
+  int lt = t0, lc = cb;
+  if (nitems > 0) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      issue(ring[k], lt, lc);
+      advance(lt, lc);
+    }
+  }
+
+  stage_slots<4>(
+      tid, NW * kWave, M * S8,
+      [&](int t) {
+        const uint16_t* src = x + (t / S8) * ldx + (t % S8) * 8;
+        if (x_vec16) return *reinterpret_cast<const uint4*>(src);
+        return make_uint4(src[0] | ((uint32_t)src[1] << 16), src[2] | ((uint32_t)src[3] << 16),
+                          src[4] | ((uint32_t)src[5] << 16), src[6] | ((uint32_t)src[7] << 16));
+      },
+      [&](int t, uint4 v) {
+        const int m = t / S8;
+        xs[m * S8 + ((t - m * S8) ^ ((m & 3) << 2))] = v;
+      });
+  __syncthreads();
+
+  uint32_t aoff[4];
+  const int arow = n < M ? n : n % M;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    aoff[t] = (uint32_t)((arow * S8 + ((4 * t + g) ^ ((arow & 3) << 2))) * 16);
+  const char* xs_bytes = reinterpret_cast<const char*>(xs);
+
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = zero4;
+  auto consume = [&](const Item& cur, int tile, int c) {
+    const uint32_t ibase = (uint32_t)c * 256u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint4 a = *reinterpret_cast<const uint4*>(xs_bytes + (aoff[t] + ibase));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(a), bitcast<bf16x8>(cur.w[t]),
+                                                    acc, 0, 0, 0);
+    }
+    if (c == ce - 1) {  // tile finished: lane (n, g) holds rows 4g..4g+3 of column n
+      const int row = tile * 16 + n;
+      if constexpr (SPLIT) {
+        f32x4* red = reinterpret_cast<f32x4*>(xs + M * S8);  // [NW][64]
+        red[wave * kWave + lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+          f32x4 sum = red[lane];
+#pragma unroll
+          for (int v = 1; v < NW; ++v) {
+            const f32x4 o = red[v * kWave + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum[i] += o[i];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 4 * g + i;
+            if (m < M && row < N) store_out(y, m * ldy + row, sum[i], y_type);
+          }
+        }
+        __syncthreads();
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * g + i;
+          if (m < M && row < N) store_out(y, m * ldy + row, acc[i], y_type);
+        }
+      }
+      acc = zero4;
+    }
+    // Keep the scheduler from hoisting later items' A reads (16 registers
+    // each) above this one.
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int pt = t0, pc = cb;
+  int u = 0;
+#pragma unroll 1
+  for (; u + D <= nitems; u += D) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      consume(ring[k], pt, pc);
+      advance(pt, pc);
+      issue(ring[k], lt, lc);
+      advance(lt, lc);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    if (u + k < nitems) {
+      consume(ring[k], pt, pc);
+      advance(pt, pc);
+    }
+  }
+}
+
+// Launch shapes (waves per workgroup, items in flight per lane) for whole
+// tiles per wave and for tiles split over the waves of a workgroup (short
+// matrices); measured on the 1536 x 6912, 6912 x 1536 and 1536 x 1536 shapes.
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaDepth = 2;
+constexpr int kSplitWaves = 8;
+constexpr int kSplitDepth = 2;
+
+template <int M, bool SPLIT, int NW, int D>
+hipError_t launch_mfma_cfg(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
+                           int64_t ldy, int y_type, int N, int K, size_t shmem,
+                           hipStream_t stream) {
+  const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
+  const int ntiles = (N + 15) / 16;
+  auto kern = bf16_gemv_mfma<M, SPLIT, NW, D>;
+  const hipError_t e = allow_lds(kern, shmem);
+  if (e != hipSuccess) return e;
+  const int cap = resident_workgroups(kern, NW * kWave, shmem);
+  const int want = SPLIT ? ntiles : (ntiles + NW - 1) / NW;
+  const int grid = want < cap ? want : cap;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * kWave), shmem, stream, x, ldx, w, ldw, y, ldy,
+                     y_type, N, K, ntiles, x_vec16);
+  return hipGetLastError();
+}
+
+// Whole tiles per wave when the tiles fill at least half of the resident
+// wavefront slots; otherwise the waves of a workgroup split each tile.
+template <int M>
+hipError_t launch_mfma(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
+                       int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
+  const size_t xbytes = (size_t)M * K * 2;
+  const int ntiles = (N + 15) / 16;
+  auto whole = bf16_gemv_mfma<M, false, kMfmaWaves, kMfmaDepth>;
+  const hipError_t e = allow_lds(whole, xbytes);
+  if (e != hipSuccess) return e;
+  const int64_t waves = (int64_t)resident_workgroups(whole, kMfmaWaves * kWave, xbytes) * kMfmaWaves;
+  // Split: every wave needs at least one item of the tile, and the partial
+  // sums (16 bytes per lane) share LDS with x.
+  const size_t split_bytes = xbytes + (size_t)kSplitWaves * kWave * 16;
+  if (2LL * ntiles < waves && K / 128 >= kSplitWaves && split_bytes <= (size_t)kLdsMax)
+    return launch_mfma_cfg<M, true, kSplitWaves, kSplitDepth>(x, ldx, w, ldw, y, ldy, y_type, N,
+                                                             K, split_bytes, stream);
+  return launch_mfma_cfg<M, false, kMfmaWaves, kMfmaDepth>(x, ldx, w, ldw, y, ldy, y_type, N, K,
+                                                          xbytes, stream);
+}
+
 template <int M, int LPR, int R>
 hipError_t launch_aligned(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
                           int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
@@ -205,12 +403,19 @@ hipError_t launch_general(const uint16_t* x, int64_t ldx, const uint16_t* w, int
   return hipGetLastError();
 }
 
+// Smallest M that takes the matrix-core kernel.
+constexpr int kMfmaMinM = 2;
+
 template <int M>
 hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
                     int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
   const bool aligned = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0) &&
                        ((reinterpret_cast<uintptr_t>(w) & 15) == 0) && (ldw % 8 == 0) &&
                        (K % 8 == 0);
+  if constexpr (M >= kMfmaMinM) {
+    if (aligned && K % 128 == 0 && (size_t)M * K * 2 <= (size_t)kLdsMax)
+      return launch_mfma<M>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
+  }
   // 16 lanes per row, widened for short matrices (see widen_lanes_per_row).
   const int lpr = widen_lanes_per_row(16, N, (K + 7) / 8);
   constexpr int R = (M <= 4) ? 2 : 1;

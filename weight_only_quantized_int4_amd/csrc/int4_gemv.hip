@@ -60,6 +60,20 @@ __device__ __forceinline__ Pairs8 unpack8(uint32_t word, uint32_t magic, uint32_
   return r;
 }
 
+// Eight consecutive halves of x (one 16-byte load when x is 16-byte aligned
+// with a row stride that keeps it so).
+__device__ __forceinline__ uint4 load_x8(const uint16_t* src, int vec16) {
+  if (vec16) return *reinterpret_cast<const uint4*>(src);
+  return make_uint4(src[0] | ((uint32_t)src[1] << 16), src[2] | ((uint32_t)src[3] << 16),
+                    src[4] | ((uint32_t)src[5] << 16), src[6] | ((uint32_t)src[7] << 16));
+}
+
+// x0..x7 -> (x0,x4 | x1,x5 | x2,x6 | x3,x7), the order of unpack8's pairs.
+__device__ __forceinline__ uint4 pair_halves(uint4 v) {
+  return make_uint4((v.x & 0xFFFFu) | (v.z << 16), (v.x >> 16) | (v.z & 0xFFFF0000u),
+                    (v.y & 0xFFFFu) | (v.w << 16), (v.y >> 16) | (v.w & 0xFFFF0000u));
+}
+
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
@@ -131,22 +145,17 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_kernel(
 
     __syncthreads();
     const int groups = kn >> 3;
-    for (int t = tid; t < M * groups; t += kBlock) {
-      const int m = t / groups;
-      const int gi = t - m * groups;
-      const uint16_t* src = x + m * ldx + kc + gi * 8;
-      uint32_t h[8];
-      if (x_vec16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src);
-        h[0] = v.x & 0xFFFFu; h[1] = v.x >> 16; h[2] = v.y & 0xFFFFu; h[3] = v.y >> 16;
-        h[4] = v.z & 0xFFFFu; h[5] = v.z >> 16; h[6] = v.w & 0xFFFFu; h[7] = v.w >> 16;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = src[e];
-      }
-      xs[m * PS + (gi >> 2) * 5 + (gi & 3)] = make_uint4(
-          h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16), h[3] | (h[7] << 16));
-    }
+    stage_slots<4>(
+        tid, kBlock, M * groups,
+        [&](int t) {
+          const int m = t / groups;
+          return load_x8(x + m * ldx + kc + (t - m * groups) * 8, x_vec16);
+        },
+        [&](int t, uint4 v) {
+          const int m = t / groups;
+          const int gi = t - m * groups;
+          xs[m * PS + (gi >> 2) * 5 + (gi & 3)] = pair_halves(v);
+        });
     __syncthreads();
 
 #pragma unroll 1
@@ -281,22 +290,17 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
   if (nitems > 0) load(cur, t_begin, 0);
 
   const int groups = K >> 3;
-  for (int t = tid; t < M * groups; t += kBlock) {
-    const int m = t / groups;
-    const int gi = t - m * groups;
-    const uint16_t* src = x + m * ldx + gi * 8;
-    uint32_t h[8];
-    if (x_vec16) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
-      h[0] = v.x & 0xFFFFu; h[1] = v.x >> 16; h[2] = v.y & 0xFFFFu; h[3] = v.y >> 16;
-      h[4] = v.z & 0xFFFFu; h[5] = v.z >> 16; h[6] = v.w & 0xFFFFu; h[7] = v.w >> 16;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = src[e];
-    }
-    xs[m * PS + (gi >> 2) * 5 + (gi & 3)] = make_uint4(
-        h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16), h[3] | (h[7] << 16));
-  }
+  stage_slots<4>(
+      tid, kBlock, M * groups,
+      [&](int t) {
+        const int m = t / groups;
+        return load_x8(x + m * ldx + (t - m * groups) * 8, x_vec16);
+      },
+      [&](int t, uint4 v) {
+        const int m = t / groups;
+        const int gi = t - m * groups;
+        xs[m * PS + (gi >> 2) * 5 + (gi & 3)] = pair_halves(v);
+      });
   __syncthreads();
 
   float acc[R][M];
@@ -488,23 +492,17 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     }
   }
 
-  for (int t = tid; t < M * S8; t += NW * kWave) {
-    const int m = t / S8;
-    const int gi = t - m * S8;
-    const uint16_t* src = x + m * ldx + gi * 8;
-    uint32_t h[8];
-    if (x_vec16) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
-      h[0] = v.x & 0xFFFFu; h[1] = v.x >> 16; h[2] = v.y & 0xFFFFu; h[3] = v.y >> 16;
-      h[4] = v.z & 0xFFFFu; h[5] = v.z >> 16; h[6] = v.w & 0xFFFFu; h[7] = v.w >> 16;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = src[e];
-    }
-    xs[m * S8 + (gi ^ ((m & 3) << kSwzShift))] =
-        make_uint4(h[0] | (h[4] << 16), h[1] | (h[5] << 16), h[2] | (h[6] << 16),
-                   h[3] | (h[7] << 16));
-  }
+  stage_slots<4>(
+      tid, NW * kWave, M * S8,
+      [&](int t) {
+        const int m = t / S8;
+        return load_x8(x + m * ldx + (t - m * S8) * 8, x_vec16);
+      },
+      [&](int t, uint4 v) {
+        const int m = t / S8;
+        const int gi = t - m * S8;
+        xs[m * S8 + (gi ^ ((m & 3) << kSwzShift))] = pair_halves(v);
+      });
   __syncthreads();
 
   // LDS byte address of the A slot that MFMA t of item 0 reads (rows >= M

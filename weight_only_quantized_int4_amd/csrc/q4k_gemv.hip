@@ -132,12 +132,19 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
     __syncthreads();
     if (x_vec16) {
       const int v4 = kn >> 2;
-      for (int t = tid; t < M * v4; t += NT) {
-        const int m = t / v4, i = t - m * v4;
-        const int e = 4 * i;
-        *reinterpret_cast<float4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) =
-            *reinterpret_cast<const float4*>(x + m * ldx + kc + e);
-      }
+      // one slot in flight: this kernel's M accumulators per row already use
+      // the register file
+      stage_slots<1>(
+          tid, NT, M * v4,
+          [&](int t) {
+            const int m = t / v4;
+            return *reinterpret_cast<const uint4*>(x + m * ldx + kc + 4 * (t - m * v4));
+          },
+          [&](int t, uint4 v) {
+            const int m = t / v4;
+            const int e = 4 * (t - m * v4);
+            *reinterpret_cast<uint4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) = v;
+          });
     } else {
       for (int t = tid; t < M * kn; t += NT) {
         const int m = t / kn, i = t - m * kn;
@@ -309,15 +316,23 @@ void q4k_gemv_persistent(
   // Stage x; the chunk sums come out of the same pass when x is 16-byte
   // aligned (8 consecutive lanes hold one 32-element chunk).
   if (x_vec16) {
+    // K is a multiple of 256, so M * K / 4 is a multiple of 64: whole
+    // wavefronts stage together and the 8-lane DPP sum is well defined.
     const int v4 = K >> 2;
-    for (int t = tid; t < M * v4; t += NT) {
-      const int m = t / v4, i = t - m * v4;
-      const int e = 4 * i;
-      const float4 v = *reinterpret_cast<const float4*>(x + m * ldx + e);
-      *reinterpret_cast<float4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) = v;
-      const float part = group_sum<8>((v.x + v.y) + (v.z + v.w));
-      if ((i & 7) == 0) sx[m * K32 + (i >> 3)] = part;
-    }
+    stage_slots<4>(
+        tid, NT, M * v4,
+        [&](int t) {
+          const int m = t / v4;
+          return *reinterpret_cast<const uint4*>(x + m * ldx + 4 * (t - m * v4));
+        },
+        [&](int t, uint4 u) {
+          const int m = t / v4, i = t - m * v4;
+          const int e = 4 * i;
+          const float4 v = bitcast<float4>(u);
+          *reinterpret_cast<float4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) = v;
+          const float part = group_sum<8>((v.x + v.y) + (v.z + v.w));
+          if ((i & 7) == 0) sx[m * K32 + (i >> 3)] = part;
+        });
     __syncthreads();
   } else {
     for (int t = tid; t < M * K; t += NT) {
@@ -514,9 +529,11 @@ hipError_t launch_q4k_gemv(const float* x, int64_t ldx, const uint8_t* w, const 
   // When x (all M rows) does not fit in a workgroup's LDS but a few rows do,
   // run the persistent kernel on groups of rows: each group re-reads the
   // weights, which beats restaging x for every 4 rows in the tiled kernel.
+  // Rows too long for LDS go to the K-chunked tiled kernel, at most 4 rows of
+  // x at a time (its per-row accumulators would spill beyond that).
   const size_t per_row = ((size_t)(K / 64) * 68 + K / 32) * 4;
-  const int mfit = (int)((size_t)kLdsMax / per_row);
-  if (M > mfit && mfit >= 1) {
+  const int mfit = (size_t)kLdsMax >= per_row ? (int)((size_t)kLdsMax / per_row) : (M < 4 ? M : 4);
+  if (M > mfit) {
     for (int m0 = 0; m0 < M; m0 += mfit) {
       const int mm = M - m0 < mfit ? M - m0 : mfit;
       const hipError_t e = launch_q4k_gemv(x + m0 * ldx, ldx, w, dsc, y + m0 * ldy, ldy, mm, N,

@@ -11,6 +11,7 @@ namespace qg {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -58,6 +59,30 @@ __device__ __forceinline__ uint32_t vreg_copy(uint32_t v) {
   uint32_t r;
   asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
   return r;
+}
+
+// Stage `count` 16-byte slots into LDS: slot t is read by load(t) and
+// written by store(t, v).  Each thread keeps up to U independent loads in
+// flight before its first wait, so staging costs one memory round trip per U
+// slots of a thread instead of one per slot.  Threads whose slot index runs
+// past `count` skip it (the stores may use wave-wide DPP only when `count`
+// is a multiple of 64).
+template <int U, typename Load, typename Store>
+__device__ __forceinline__ void stage_slots(int tid, int nthreads, int count, Load load,
+                                            Store store) {
+  for (int t0 = tid; t0 < count; t0 += nthreads * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * nthreads;
+      if (t < count) v[u] = load(t);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * nthreads;
+      if (t < count) store(t, v[u]);
+    }
+  }
 }
 
 // DPP lane permutes within a row of 16 lanes.
