@@ -83,6 +83,24 @@ def test_m_sweep(M):
     assert np.array_equal(yd, y_host(y2))
 
 
+@pytest.mark.parametrize("N,K", [(9001, 4096), (1003, 11008), (300, 8192)])
+def test_m1_rows_and_pieces_per_lane(N, K):
+    # M = 1: rows past one resident round of wavefronts (9001 x 4096), and 3
+    # (K = 11008) or 2 (K = 8192) pieces of a row per lane, with ragged row
+    # counts and last strides
+    p = q4k_case(N, K, 424)
+    yr, S = q4k_ref(N, K, 424)
+    xd, wd = to_dev(p.x[:1]), to_dev(p.w)
+    say(f"q4k M=1 N={N} K={K}")
+    y = torch.full((1, N), float("nan"), device=DEV)
+    q.qgemv_q4k(xd, wd, y)
+    yd = y_host(y)
+    assert_accept(yd, yr[:1], S[:1], "f32", f"q4k M=1 {N}x{K}")
+    y2 = torch.full((1, N), float("nan"), device=DEV)
+    q.qgemv_q4k_dsc(xd, wd, _plane(wd, N, K), y2)
+    assert np.array_equal(yd, y_host(y2))
+
+
 @pytest.mark.parametrize("M", [2, 3])
 def test_long_rows_x_resident(M):
     # K = 11008: x and its chunk sums take 94 KB (M = 2) and 141 KB (M = 3) of

@@ -58,7 +58,6 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
       for (int i = 0; i < R; ++i) v[i] = load_stream16(w + (wo[i] + (uint32_t)(kc + 8 * p)));
     };
     uint4 cur[R];
-    if (j < P) load(cur, j);
     __syncthreads();
     stage_slots<4>(
         tid, kBlock, M * P,
@@ -69,6 +68,9 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
         [&](int t, uint4 v) {
           const int m = t / P;
           xs[m * G + (t - m * P)] = v;
+        },
+        [&] {
+          if (j < P) load(cur, j);
         });
     __syncthreads();
 #pragma unroll 1
@@ -236,14 +238,6 @@ __global__ __launch_bounds__(NW * kWave) void bf16_gemv_mfma(
 
   Item ring[D];
   int lt = t0, lc = cb;
-  if (nitems > 0) {
-#pragma unroll
-    for (int k = 0; k < D; ++k) {
-      issue(ring[k], lt, lc);
-      advance(lt, lc);
-    }
-  }
-
   stage_slots<4>(
       tid, NW * kWave, M * S8,
       [&](int t) {
@@ -255,6 +249,13 @@ __global__ __launch_bounds__(NW * kWave) void bf16_gemv_mfma(
       [&](int t, uint4 v) {
         const int m = t / S8;
         xs[m * S8 + ((t - m * S8) ^ ((m & 3) << 2))] = v;
+      },
+      [&] {  // unconditional: rows past the end are clamped
+#pragma unroll
+        for (int k = 0; k < D; ++k) {
+          issue(ring[k], lt, lc);
+          advance(lt, lc);
+        }
       });
   __syncthreads();
 

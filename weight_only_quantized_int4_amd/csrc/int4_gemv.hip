@@ -138,11 +138,9 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_kernel(
     const int kn = min(KC, K - kc);
     const int P = kn >> 5;
     const int gp0 = kc >> 5;
-    // Issue the first piece's loads before staging x: their latency overlaps
-    // the staging and the barrier.
+    // The first piece's loads go out right behind the x loads: their latency
+    // overlaps the staging and the barrier.
     Piece<R> cur;
-    if (j < P) load(cur, gp0 + j);
-
     __syncthreads();
     const int groups = kn >> 3;
     stage_slots<4>(
@@ -155,6 +153,9 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_kernel(
           const int m = t / groups;
           const int gi = t - m * groups;
           xs[m * PS + (gi >> 2) * 5 + (gi & 3)] = pair_halves(v);
+        },
+        [&] {
+          if (j < P) load(cur, gp0 + j);
         });
     __syncthreads();
 
@@ -287,8 +288,6 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
 
   const int nitems = my_tiles * PPI;
   Item<R, PB> cur;
-  if (nitems > 0) load(cur, t_begin, 0);
-
   const int groups = K >> 3;
   stage_slots<4>(
       tid, kBlock, M * groups,
@@ -300,7 +299,8 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
         const int m = t / groups;
         const int gi = t - m * groups;
         xs[m * PS + (gi >> 2) * 5 + (gi & 3)] = pair_halves(v);
-      });
+      },
+      [&] { load(cur, t_begin, 0); });  // rows past the end are clamped
   __syncthreads();
 
   float acc[R][M];
@@ -484,14 +484,6 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
 
   Group ring[DG];
   int lt = t0, lgc = cb;  // next group to load
-  if (ngroups > 0) {
-#pragma unroll
-    for (int k = 0; k < DG; ++k) {
-      issue(ring[k], lt, lgc);
-      advance(lt, lgc);
-    }
-  }
-
   stage_slots<4>(
       tid, NW * kWave, M * S8,
       [&](int t) {
@@ -502,6 +494,13 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
         const int m = t / S8;
         const int gi = t - m * S8;
         xs[m * S8 + (gi ^ ((m & 3) << kSwzShift))] = pair_halves(v);
+      },
+      [&] {  // unconditional: rows past the end are clamped
+#pragma unroll
+        for (int k = 0; k < DG; ++k) {
+          issue(ring[k], lt, lgc);
+          advance(lt, lgc);
+        }
       });
   __syncthreads();
 

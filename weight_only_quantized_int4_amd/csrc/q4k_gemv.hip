@@ -125,9 +125,11 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
     const int kn = min(KC, K - kc);
     const int P = kn >> 6;  // (super-block, g) pieces in this chunk
     const int sb0 = kc >> 8;
-    // First piece's loads go out before x is staged.
+    // The first piece's loads go out right behind the first x loads.
     Q4kPiece cur;
-    if (j < P) load(cur, sb0 + (j >> 2));
+    auto first_piece = [&] {
+      if (j < P) load(cur, sb0 + (j >> 2));
+    };
 
     __syncthreads();
     if (x_vec16) {
@@ -144,8 +146,10 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
             const int m = t / v4;
             const int e = 4 * (t - m * v4);
             *reinterpret_cast<uint4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) = v;
-          });
+          },
+          first_piece);
     } else {
+      first_piece();
       for (int t = tid; t < M * kn; t += NT) {
         const int m = t / kn, i = t - m * kn;
         xs[m * XSTR + (i >> 6) * 68 + (i & 63)] = x[m * ldx + kc + i];
@@ -241,10 +245,11 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
 // contiguous share of rows among its wavefronts.  A wavefront owns one row at
 // a time (LPR = 64) and walks a flat sequence of (row, piece) items with a
 // register ring of D items that crosses row boundaries.
-// M = 1 with 1024-thread workgroups asks for 64 VGPRs (8 wavefronts per SIMD),
-// so that two workgroups share a CU.
+// M = 1 with 1024-thread workgroups and a ring of at most 2 items asks for 64
+// VGPRs (8 wavefronts per SIMD), so that two workgroups share a CU.
 template <int M, int NT, bool DSC, bool STRIDED, int D>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(M == 1 && NT == 1024 ? 8 : 1)))
+__global__ __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(M == 1 && NT == 1024 && D <= 2 ? 8 : 1)))
 void q4k_gemv_persistent(
     const float* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const float2* __restrict__ dsc, float* __restrict__ y, int64_t ldy, int N, int K,
@@ -305,21 +310,24 @@ void q4k_gemv_persistent(
   // clamped, so surplus loads re-read cached bytes).
   Q4kPiece ring[D];
   int lrow = first, lit = 0;  // next item to load
-  if (nitems > 0) {
+  // (unconditional: a wavefront without rows loads clamped ones and never
+  // consumes them)
+  auto fill_ring = [&] {
 #pragma unroll
     for (int k = 0; k < D; ++k) {
       load(ring[k], lrow, lit);
       advance(lrow, lit);
     }
-  }
+  };
 
   // Stage x; the chunk sums come out of the same pass when x is 16-byte
-  // aligned (8 consecutive lanes hold one 32-element chunk).
+  // aligned (8 consecutive lanes hold one 32-element chunk).  The ring's
+  // first loads go out right behind the first x loads.
   if (x_vec16) {
     // K is a multiple of 256, so M * K / 4 is a multiple of 64: whole
     // wavefronts stage together and the 8-lane DPP sum is well defined.
     const int v4 = K >> 2;
-    stage_slots<4>(
+    stage_slots<2>(
         tid, NT, M * v4,
         [&](int t) {
           const int m = t / v4;
@@ -332,9 +340,11 @@ void q4k_gemv_persistent(
           *reinterpret_cast<float4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) = v;
           const float part = group_sum<8>((v.x + v.y) + (v.z + v.w));
           if ((i & 7) == 0) sx[m * K32 + (i >> 3)] = part;
-        });
+        },
+        fill_ring);
     __syncthreads();
   } else {
+    fill_ring();
     for (int t = tid; t < M * K; t += NT) {
       const int m = t / K, i = t - m * K;
       xs[m * XSTR + (i >> 6) * 68 + (i & 63)] = x[m * ldx + i];
@@ -478,8 +488,27 @@ __global__ __launch_bounds__(kBlock) void q4k_plane_kernel(const uint8_t* __rest
 }
 
 constexpr bool kQ4kStrided = false;
-// Items (64-weight pieces) in flight per lane in the persistent kernel.
-constexpr int kQ4kDepth = 1;
+
+// One persistent launch with a ring of D items per lane: each wavefront gets
+// D / PPI rows (at least one), so that all of its items can be in flight at
+// once; the grid is capped at one resident round.
+template <int M, int NT, int D>
+hipError_t launch_persistent(const float* x, int64_t ldx, const uint8_t* w, const float2* dsc2,
+                             float* y, int64_t ldy, int N, int K, int x_vec16, size_t full, int PPI,
+                             hipStream_t stream) {
+  auto kern = dsc2 ? q4k_gemv_persistent<M, NT, true, kQ4kStrided, D>
+                   : q4k_gemv_persistent<M, NT, false, kQ4kStrided, D>;
+  const hipError_t e = allow_lds(kern, full);
+  if (e != hipSuccess) return e;
+  const int cap = resident_workgroups(kern, NT, full);
+  const int rows_per_wave = D / PPI > 1 ? D / PPI : 1;
+  const int rows_per_wg = (NT / kWave) * rows_per_wave;
+  const int want = (N + rows_per_wg - 1) / rows_per_wg;
+  const int grid = want < cap ? want : cap;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), full, stream, x, ldx, w, dsc2, y, ldy, N, K,
+                     x_vec16);
+  return hipGetLastError();
+}
 
 // Persistent kernel (1024 threads: 16 rows in flight per workgroup, x staged
 // once) whenever x and its chunk sums fit in a workgroup's LDS (up to 160 KB);
@@ -494,32 +523,29 @@ hipError_t launch_m(const float* x, int64_t ldx, const uint8_t* w, const float* 
   // x (68 floats per 64 elements) plus its chunk sums (2 floats per 64), fp32.
   const size_t full = (size_t)M * ((K / 64) * 68 + K / 32) * 4;
   if (full <= (size_t)kLdsMax) {
-    constexpr int D = M == 1 ? kQ4kDepth : 1;
-    auto kern = dsc ? q4k_gemv_persistent<M, NT, true, kQ4kStrided, D>
-                    : q4k_gemv_persistent<M, NT, false, kQ4kStrided, D>;
-    const hipError_t e = allow_lds(kern, full);
-    if (e != hipSuccess) return e;
-    const int cap = resident_workgroups(kern, NT, full);
-    const int rows_per_wg = NT / kWave;
-    const int want = (N + rows_per_wg - 1) / rows_per_wg;
-    const int grid = want < cap ? want : cap;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), full, stream, x, ldx, w, dsc2, y, ldy, N, K,
-                       x_vec16);
+    // One item per lane in flight over a full grid measured faster than
+    // deeper rings on fewer workgroups (4096 x 11008 and 11008 x 4096, M = 1).
+    return launch_persistent<M, NT, 1>(x, ldx, w, dsc2, y, ldy, N, K, x_vec16, full, 1, stream);
+  }
+  // The tiled kernel is launched for at most 4 rows of x (launch_q4k_gemv
+  // splits larger M into row groups), so only M <= 4 is instantiated.
+  if constexpr (M > 4) {
+    return hipErrorInvalidValue;
+  } else {
+    constexpr int S = NT_TILED / LPR;
+    const int grid = (N + S - 1) / S;
+    // KC a multiple of 256 (whole super-blocks) within the LDS budget.
+    int KC = (kLdsBudget / (4 * 70 * M)) * 64 & ~255;
+    if (KC > K) KC = K;
+    const size_t shmem = (size_t)M * ((KC / 64) * 68 + KC / 32) * 4;
+    if (dsc)
+      hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT_TILED, true>), dim3(grid), dim3(NT_TILED),
+                         shmem, stream, x, ldx, w, dsc2, y, ldy, N, K, KC, x_vec16);
+    else
+      hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT_TILED, false>), dim3(grid), dim3(NT_TILED),
+                         shmem, stream, x, ldx, w, nullptr, y, ldy, N, K, KC, x_vec16);
     return hipGetLastError();
   }
-  constexpr int S = NT_TILED / LPR;
-  const int grid = (N + S - 1) / S;
-  // KC a multiple of 256 (whole super-blocks) within the LDS budget.
-  int KC = (kLdsBudget / (4 * 70 * M)) * 64 & ~255;
-  if (KC > K) KC = K;
-  const size_t shmem = (size_t)M * ((KC / 64) * 68 + KC / 32) * 4;
-  if (dsc)
-    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT_TILED, true>), dim3(grid), dim3(NT_TILED),
-                       shmem, stream, x, ldx, w, dsc2, y, ldy, N, K, KC, x_vec16);
-  else
-    hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT_TILED, false>), dim3(grid), dim3(NT_TILED),
-                       shmem, stream, x, ldx, w, nullptr, y, ldy, N, K, KC, x_vec16);
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -64,25 +64,51 @@ __device__ __forceinline__ uint32_t vreg_copy(uint32_t v) {
 // Stage `count` 16-byte slots into LDS: slot t is read by load(t) and
 // written by store(t, v).  Each thread keeps up to U independent loads in
 // flight before its first wait, so staging costs one memory round trip per U
-// slots of a thread instead of one per slot.  Threads whose slot index runs
-// past `count` skip it (the stores may use wave-wide DPP only when `count`
-// is a multiple of 64).
-template <int U, typename Load, typename Store>
+// slots of a thread instead of one per slot.
+//
+// `first` runs once per thread right after the first round of x loads is
+// issued and before anything waits on them: kernels issue their first weight
+// loads there.  Loads complete in issue order as far as the wait counter is
+// concerned, so weight loads issued before the x loads would make the first
+// x store wait for the weights (a full HBM round trip) as well.
+//
+// Loads and stores are unconditional (a slot index past `count` re-reads and
+// rewrites the last slot with the same value; count >= 1): no branch sits
+// between the x loads and `first`'s loads and nothing sinks the x loads
+// behind them, so the wait before the first store covers the x loads only.
+// A store that combines lanes (DPP) sees whole wavefronts either in range or
+// all clamped when `count` is a multiple of 64.
+template <int U, typename Load, typename Store, typename First>
 __device__ __forceinline__ void stage_slots(int tid, int nthreads, int count, Load load,
-                                            Store store) {
-  for (int t0 = tid; t0 < count; t0 += nthreads * U) {
+                                            Store store, First first) {
+  bool pending = true;
+  for (int t0 = tid; t0 < count || pending; t0 += nthreads * U) {
     uint4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * nthreads;
-      if (t < count) v[u] = load(t);
+      v[u] = load(t < count ? t : count - 1);
+    }
+    if (pending) {
+      // keep the scheduler from moving x loads behind `first`'s loads (or
+      // x stores ahead of them)
+      __builtin_amdgcn_sched_barrier(0);
+      first();
+      __builtin_amdgcn_sched_barrier(0);
+      pending = false;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * nthreads;
-      if (t < count) store(t, v[u]);
+      store(t < count ? t : count - 1, v[u]);
     }
   }
+}
+
+template <int U, typename Load, typename Store>
+__device__ __forceinline__ void stage_slots(int tid, int nthreads, int count, Load load,
+                                            Store store) {
+  stage_slots<U>(tid, nthreads, count, load, store, [] {});
 }
 
 // DPP lane permutes within a row of 16 lanes.
