@@ -188,6 +188,29 @@ const char *qg_status_string(qg_status s);
  * same thread. */
 const char *qg_last_error(void);
 
+/*
+ * Liveness and explain trace (for callers that dispatch on top of this
+ * library).  A fast path that degrades correctly must carry a visible label,
+ * because parity cannot see which path ran ("62 . r59 -- q4_K W_dsc plane +
+ * riders", section 3.1, "Failure must be loud"; section 4, liveness).
+ *
+ * qg_last_launch   : the kernels enqueued by the calling thread's last library
+ *                    call, as "path M=.. grid=.. block=.. lds=.." entries
+ *                    separated by "; " ("" if it enqueued nothing).  The
+ *                    string is thread-local storage owned by the library,
+ *                    valid until the thread's next call.
+ * qg_path_count    : number of kernel paths.
+ * qg_path_name     : the name of path i (NULL when out of range); static
+ *                    storage.
+ * qg_path_launches : launches of path i since the library was loaded (all
+ *                    threads; 0 when out of range).
+ * Host-only; none of these touches the GPU.
+ */
+const char *qg_last_launch(void);
+int32_t qg_path_count(void);
+const char *qg_path_name(int32_t path);
+uint64_t qg_path_launches(int32_t path);
+
 #ifdef __cplusplus
 }
 #endif

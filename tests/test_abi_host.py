@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert names == sorted(["qgemv_int4_blockwise", "qgemv_q4k", "qgemv_q4k_dsc", "gemv_bf16",
                             "q4k_dsc_plane_bytes", "q4k_build_dsc_plane", "qg_status_string",
-                            "qg_last_error"])
+                            "qg_last_error", "qg_last_launch", "qg_path_count", "qg_path_name",
+                            "qg_path_launches"])
 
 
 def test_library_exports_exactly_the_header():
@@ -182,3 +183,16 @@ def test_product_package_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def test_liveness_exports_on_the_host():
+    # host-only functions: no GPU needed
+    names = q.path_names()
+    assert len(names) == q.load_library().qg_path_count() == 13
+    assert names[0] == "int4_dot2_persistent" and "q4k_persistent_plane" in names
+    assert q.load_library().qg_path_name(-1) is None
+    assert q.load_library().qg_path_name(len(names)) is None
+    assert q.load_library().qg_path_launches(len(names)) == 0
+    counts = q.path_launches()
+    assert set(counts) == set(names) and all(v >= 0 for v in counts.values())
+    assert isinstance(q.last_launch(), str)

@@ -1,0 +1,118 @@
+"""Host-side logic of the dispatch layer (no GPU): plane registry, liveness
+labels, the once-per-process fallback warning, the QGEMV_Q4K_DSC switch and
+row groups.  The C-ABI calls are replaced by recorders; the GPU behaviour is
+covered by tests/test_gpu_dispatch.py."""
+import warnings
+
+import pytest
+import torch
+
+from weight_only_quantized_int4_amd import dispatch, qgemv
+
+
+@pytest.fixture
+def fake_abi(monkeypatch):
+    calls = []
+
+    def q4k(x, w, y, stream=None):
+        calls.append(("q4k", x.shape[0]))
+        return y
+
+    def q4k_dsc(x, w, dsc, y, stream=None):
+        assert dsc is not None
+        calls.append(("q4k_dsc", x.shape[0]))
+        return y
+
+    def build(w, dsc, N, K, stream=None):
+        calls.append(("build", N, K))
+        return dsc
+
+    def int4(x, w, s, z, y, bs, stream=None):
+        calls.append(("int4", x.shape[0], y.shape[0]))
+        return y
+
+    def bf16(x, w, y, stream=None):
+        calls.append(("bf16", x.shape[0], y.shape[0]))
+        return y
+
+    monkeypatch.setattr(qgemv, "qgemv_q4k", q4k)
+    monkeypatch.setattr(qgemv, "qgemv_q4k_dsc", q4k_dsc)
+    monkeypatch.setattr(qgemv, "q4k_build_dsc_plane", build)
+    monkeypatch.setattr(qgemv, "q4k_dsc_plane_bytes", lambda N, K: N * K // 4)
+    monkeypatch.setattr(qgemv, "qgemv_int4_blockwise", int4)
+    monkeypatch.setattr(qgemv, "gemv_bf16", bf16)
+    monkeypatch.delenv("QGEMV_Q4K_DSC", raising=False)
+    dispatch.reset_liveness()
+    yield calls
+    dispatch.reset_liveness()
+
+
+def _q4k_weights(N=16, K=512):
+    return torch.zeros((N, K // 256 * 144), dtype=torch.uint8)
+
+
+def test_plane_label_and_row_groups(fake_abi):
+    w = _q4k_weights()
+    assert dispatch.register_q4k_plane(w)
+    assert fake_abi[-1] == ("build", 16, 512)
+    assert dispatch.q4k_plane_of(w).shape == (16 * 512 // 4 // 8, 2)
+    x = torch.zeros((19, 512))
+    y, label = dispatch.q4k_linear(x, w)
+    assert label == dispatch.LABEL_PLANE and y.shape == (19, 16)
+    assert fake_abi[-3:] == [("q4k_dsc", 8), ("q4k_dsc", 8), ("q4k_dsc", 3)]
+    assert dispatch.liveness()[dispatch.LABEL_PLANE] == 1
+    dispatch.unregister_q4k_plane(w)
+    _, label = dispatch.q4k_linear(x[:1], w)
+    assert label == dispatch.LABEL_OFF and fake_abi[-1] == ("q4k", 1)
+
+
+def test_switched_off_plane(fake_abi, monkeypatch):
+    w = _q4k_weights()
+    assert dispatch.register_q4k_plane(w)
+    monkeypatch.setenv("QGEMV_Q4K_DSC", "0")
+    _, label = dispatch.q4k_linear(torch.zeros((2, 512)), w)
+    assert label == dispatch.LABEL_OFF and fake_abi[-1] == ("q4k", 2)
+    monkeypatch.delenv("QGEMV_Q4K_DSC")
+    _, label = dispatch.q4k_linear(torch.zeros((2, 512)), w, use_plane=False)
+    assert label == dispatch.LABEL_OFF
+    _, label = dispatch.q4k_linear(torch.zeros((2, 512)), w)
+    assert label == dispatch.LABEL_PLANE
+
+
+def test_failed_registration_falls_back_loudly_once(fake_abi, monkeypatch):
+    w = _q4k_weights()
+
+    def failing_build(w, dsc, N, K, stream=None):
+        raise qgemv.QgemvError("q4k_build_dsc_plane", 6, "QG_ERR_HIP", "simulated")
+
+    monkeypatch.setattr(qgemv, "q4k_build_dsc_plane", failing_build)
+    assert not dispatch.register_q4k_plane(w)
+    assert dispatch.q4k_plane_of(w) is None
+    x = torch.zeros((1, 512))
+    with warnings.catch_warnings(record=True) as got:
+        warnings.simplefilter("always")
+        _, l1 = dispatch.q4k_linear(x, w)
+        _, l2 = dispatch.q4k_linear(x, w)
+    assert l1 == l2 == dispatch.LABEL_FALLBACK
+    assert len([g for g in got if issubclass(g.category, RuntimeWarning)]) == 1
+    assert dispatch.liveness()[dispatch.LABEL_FALLBACK] == 2
+    assert fake_abi[-2:] == [("q4k", 1), ("q4k", 1)]
+
+
+def test_bad_weight_shape_is_a_failed_registration(fake_abi):
+    w = torch.zeros((4, 100), dtype=torch.uint8)  # not a multiple of 144 bytes per row
+    assert not dispatch.register_q4k_plane(w)
+
+
+@pytest.mark.parametrize("M,groups", [(1, [1]), (8, [8]), (9, [8, 1]), (20, [8, 8, 4])])
+def test_int4_and_bf16_row_groups(fake_abi, M, groups):
+    x = torch.zeros((M, 64), dtype=torch.float16)
+    w = torch.zeros((32, 32), dtype=torch.uint8)
+    y = dispatch.int4_linear(x, w, torch.zeros((32, 2), dtype=torch.float16), None, 32)
+    assert y.shape == (M, 32) and y.dtype == torch.float16
+    assert [c[1] for c in fake_abi if c[0] == "int4"] == groups
+    assert all(c[1] == c[2] for c in fake_abi if c[0] == "int4")
+    xb = torch.zeros((M, 64), dtype=torch.bfloat16)
+    yb = dispatch.bf16_linear(xb, torch.zeros((32, 64), dtype=torch.bfloat16))
+    assert yb.shape == (M, 32) and yb.dtype == torch.bfloat16
+    assert [c[1] for c in fake_abi if c[0] == "bf16"] == groups

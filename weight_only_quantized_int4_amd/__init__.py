@@ -5,7 +5,8 @@ a C ABI, see ``include/qgemv.h``).  ``qgemv`` is the thin ctypes binding with
 the same entry-point names; PyTorch only supplies device memory and streams.
 """
 from .qgemv import (  # noqa: F401
-    QG_BF16, QG_F16, QG_F32, QgemvError, gemv_bf16, library_path, load_library,
-    q4k_build_dsc_plane, q4k_dsc_plane_bytes, qgemv_int4_blockwise, qgemv_q4k,
-    qgemv_q4k_dsc,
+    QG_BF16, QG_F16, QG_F32, QgemvError, gemv_bf16, last_launch, library_path, load_library,
+    path_launches, path_names, q4k_build_dsc_plane, q4k_dsc_plane_bytes, qgemv_int4_blockwise,
+    qgemv_q4k, qgemv_q4k_dsc,
 )
+from . import dispatch  # noqa: F401

@@ -49,9 +49,30 @@ def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+    _write_build_info(out)
     if verbose:
         print(f"built {out}")
     return out
+
+
+def _write_build_info(lib: str) -> None:
+    """Record what the library was built from next to it (the GPU runs see the
+    tree without its git metadata): commit, whether the tree was dirty, and
+    the library's sha256."""
+    import hashlib
+    import json
+
+    def git(*args):
+        r = subprocess.run(["git", "-C", ROOT, *args], capture_output=True, text=True)
+        return r.stdout.strip() if r.returncode == 0 else None
+
+    with open(lib, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    info = {"git_commit": git("rev-parse", "HEAD"),
+            "git_dirty": bool(git("status", "--porcelain", "--untracked-files=no")),
+            "library_sha256": digest, "hipcc_flags": FLAGS[:-4]}
+    with open(os.path.join(PKG, "build_info.json"), "w") as f:
+        json.dump(info, f, indent=1)
 
 
 if __name__ == "__main__":

@@ -354,6 +354,7 @@ hipError_t launch_mfma_cfg(const uint16_t* x, int64_t ldx, const uint16_t* w, in
   const int grid = want < cap ? want : cap;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * kWave), shmem, stream, x, ldx, w, ldw, y, ldy,
                      y_type, N, K, ntiles, x_vec16);
+  note_launch(SPLIT ? kPathBf16MfmaSplit : kPathBf16MfmaTiles, M, grid, NW * kWave, shmem);
   return hipGetLastError();
 }
 
@@ -388,6 +389,7 @@ hipError_t launch_aligned(const uint16_t* x, int64_t ldx, const uint16_t* w, int
   const size_t shmem = (size_t)M * KC * 2;
   hipLaunchKernelGGL((bf16_gemv_aligned<M, LPR, R>), dim3(grid), dim3(kBlock), shmem, stream, x,
                      ldx, w, ldw, y, ldy, y_type, N, K, KC);
+  note_launch(kPathBf16Aligned, M, grid, kBlock, shmem);
   return hipGetLastError();
 }
 
@@ -401,6 +403,7 @@ hipError_t launch_general(const uint16_t* x, int64_t ldx, const uint16_t* w, int
   const size_t shmem = (size_t)M * (KC + 8) * 4;
   hipLaunchKernelGGL((bf16_gemv_general<M, LPR>), dim3(grid), dim3(kBlock), shmem, stream, x, ldx,
                      w, ldw, y, ldy, y_type, N, K, KC);
+  note_launch(kPathBf16General, M, grid, kBlock, shmem);
   return hipGetLastError();
 }
 

@@ -683,6 +683,7 @@ hipError_t launch_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w, const ui
     const int grid = kBalanced ? (ntiles + rounds - 1) / rounds : (ntiles < cap ? ntiles : cap);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), full, stream, x, ldx, w, scales, zp, zrow,
                        y, ldy, y_type, N, K, bs_log2, ntiles, x_vec16);
+    note_launch(kPathInt4Dot2Persistent, M, grid, kBlock, full);
     return hipGetLastError();
    }
   }
@@ -698,6 +699,7 @@ hipError_t launch_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w, const ui
     hipLaunchKernelGGL((int4_gemv_kernel<M, LPR, R, false>), dim3(grid), dim3(kBlock), shmem,
                        stream, x, ldx, w, scales, zp, zrow, y, ldy, y_type, N, K, bs_log2, KC,
                        x_vec16);
+  note_launch(kPathInt4Dot2Tiled, M, grid, kBlock, shmem);
   return hipGetLastError();
 }
 
@@ -728,6 +730,7 @@ hipError_t launch_mfma_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w,
   const int grid = want < cap ? want : cap;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * kWave), shmem, stream, x, ldx, w, scales, zp,
                      zrow, y, ldy, y_type, N, K, bs_log2, ntiles, x_vec16);
+  note_launch(SPLIT ? kPathInt4MfmaSplit : kPathInt4MfmaTiles, M, grid, NW * kWave, shmem);
   return hipGetLastError();
 }
 

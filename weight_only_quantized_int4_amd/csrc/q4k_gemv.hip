@@ -507,6 +507,7 @@ hipError_t launch_persistent(const float* x, int64_t ldx, const uint8_t* w, cons
   const int grid = want < cap ? want : cap;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), full, stream, x, ldx, w, dsc2, y, ldy, N, K,
                      x_vec16);
+  note_launch(dsc2 ? kPathQ4kPersistentPlane : kPathQ4kPersistent, M, grid, NT, full);
   return hipGetLastError();
 }
 
@@ -544,6 +545,7 @@ hipError_t launch_m(const float* x, int64_t ldx, const uint8_t* w, const float* 
     else
       hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT_TILED, false>), dim3(grid), dim3(NT_TILED),
                          shmem, stream, x, ldx, w, nullptr, y, ldy, N, K, KC, x_vec16);
+    note_launch(dsc ? kPathQ4kTiledPlane : kPathQ4kTiled, M, grid, NT_TILED, shmem);
     return hipGetLastError();
   }
 }
@@ -585,6 +587,7 @@ hipError_t launch_q4k_build_plane(const uint8_t* w, float* dsc, int N, int K, hi
   const int grid = (int)((total + kBlock - 1) / kBlock);
   hipLaunchKernelGGL(q4k_plane_kernel, dim3(grid), dim3(kBlock), 0, stream, w,
                      reinterpret_cast<float2*>(dsc), N, nsb);
+  note_launch(kPathQ4kPlaneBuild, 0, grid, kBlock, 0);
   return hipGetLastError();
 }
 

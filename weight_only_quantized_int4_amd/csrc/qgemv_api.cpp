@@ -7,6 +7,7 @@
 // human-readable detail for qg_last_error() in thread-local storage.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -18,6 +19,23 @@
 namespace {
 
 thread_local char g_last_error[512];
+
+// Liveness: per-path launch counts (process-wide) and the kernels launched by
+// the calling thread's last library call.
+std::atomic<uint64_t> g_path_launches[qg::kPathCount];
+thread_local char g_last_launch[512];
+thread_local int g_last_launch_count;
+
+const char* const kPathNames[qg::kPathCount] = {
+    "int4_dot2_persistent", "int4_dot2_tiled",   "int4_mfma_tiles",    "int4_mfma_split",
+    "q4k_persistent",       "q4k_persistent_plane", "q4k_tiled",       "q4k_tiled_plane",
+    "q4k_plane_build",      "bf16_aligned",      "bf16_mfma_tiles",    "bf16_mfma_split",
+    "bf16_general"};
+
+void begin_call() {
+  g_last_launch[0] = '\0';
+  g_last_launch_count = 0;
+}
 
 qg_status ok() {
   g_last_error[0] = '\0';
@@ -75,6 +93,20 @@ qg_status check_ld(const char* fn, const char* name, int64_t ld, int64_t need) {
 
 }  // namespace
 
+namespace qg {
+
+void note_launch(Path path, int M, int grid, int block, size_t lds) {
+  if (path < 0 || path >= kPathCount) return;
+  g_path_launches[path].fetch_add(1, std::memory_order_relaxed);
+  const size_t used = strlen(g_last_launch);
+  if (used + 1 < sizeof(g_last_launch))
+    snprintf(g_last_launch + used, sizeof(g_last_launch) - used, "%s%s M=%d grid=%d block=%d lds=%zu",
+             g_last_launch_count ? "; " : "", kPathNames[path], M, grid, block, lds);
+  ++g_last_launch_count;
+}
+
+}  // namespace qg
+
 // The library is built with hidden visibility; only the C ABI is exported.
 #pragma GCC visibility push(default)
 extern "C" {
@@ -94,10 +126,25 @@ const char* qg_status_string(qg_status s) {
 
 const char* qg_last_error(void) { return g_last_error; }
 
+const char* qg_last_launch(void) { return g_last_launch; }
+
+int32_t qg_path_count(void) { return (int32_t)qg::kPathCount; }
+
+const char* qg_path_name(int32_t path) {
+  return path >= 0 && path < qg::kPathCount ? kPathNames[path] : nullptr;
+}
+
+uint64_t qg_path_launches(int32_t path) {
+  return path >= 0 && path < qg::kPathCount
+             ? g_path_launches[path].load(std::memory_order_relaxed)
+             : 0;
+}
+
 qg_status qgemv_int4_blockwise(const uint16_t* x, int64_t ldx, const uint8_t* w,
                                const uint16_t* scales, const uint8_t* zero_points, void* y,
                                int64_t ldy, int32_t y_type, int64_t M, int64_t N, int64_t K,
                                int32_t block_size, void* stream) {
+  begin_call();
   static const char fn[] = "qgemv_int4_blockwise";
   if (!x || !w || !scales || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w, scales and y are required", fn);
   if (qg_status s = check_mnk(fn, M, N, K)) return s;
@@ -157,6 +204,7 @@ static qg_status q4k_common(const char* fn, const float* x, int64_t ldx, const u
 
 qg_status qgemv_q4k(const float* x, int64_t ldx, const uint8_t* w, float* y, int64_t ldy,
                     int64_t M, int64_t N, int64_t K, void* stream) {
+  begin_call();
   static const char fn[] = "qgemv_q4k";
   if (!x || !w || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w and y are required", fn);
   return q4k_common(fn, x, ldx, w, nullptr, y, ldy, M, N, K, stream);
@@ -164,6 +212,7 @@ qg_status qgemv_q4k(const float* x, int64_t ldx, const uint8_t* w, float* y, int
 
 qg_status qgemv_q4k_dsc(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
                         int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+  begin_call();
   static const char fn[] = "qgemv_q4k_dsc";
   if (!x || !w || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w and y are required", fn);
   if (!dsc) return fail(QG_ERR_NULL_POINTER, "%s: dsc plane is NULL (no silent fallback)", fn);
@@ -172,6 +221,7 @@ qg_status qgemv_q4k_dsc(const float* x, int64_t ldx, const uint8_t* w, const flo
 
 qg_status gemv_bf16(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
                     int64_t ldy, int32_t y_type, int64_t M, int64_t N, int64_t K, void* stream) {
+  begin_call();
   static const char fn[] = "gemv_bf16";
   if (!x || !w || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w and y are required", fn);
   if (qg_status s = check_mnk(fn, M, N, K)) return s;
@@ -202,6 +252,7 @@ size_t q4k_dsc_plane_bytes(int64_t N, int64_t K) {
 
 qg_status q4k_build_dsc_plane(const uint8_t* w, float* dsc_out, int64_t N, int64_t K,
                               void* stream) {
+  begin_call();
   static const char fn[] = "q4k_build_dsc_plane";
   if (!w || !dsc_out) return fail(QG_ERR_NULL_POINTER, "%s: w and dsc_out are required", fn);
   if (N < 0 || K < 1 || K % 256 != 0)

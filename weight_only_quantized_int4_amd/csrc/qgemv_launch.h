@@ -10,6 +10,30 @@
 
 namespace qg {
 
+// Kernel paths, for the liveness record of every launch (note_launch):
+// which kernel family ran, counted per process and described per thread.
+enum Path : int {
+  kPathInt4Dot2Persistent = 0,
+  kPathInt4Dot2Tiled,
+  kPathInt4MfmaTiles,
+  kPathInt4MfmaSplit,
+  kPathQ4kPersistent,
+  kPathQ4kPersistentPlane,
+  kPathQ4kTiled,
+  kPathQ4kTiledPlane,
+  kPathQ4kPlaneBuild,
+  kPathBf16Aligned,
+  kPathBf16MfmaTiles,
+  kPathBf16MfmaSplit,
+  kPathBf16General,
+  kPathCount
+};
+
+// Record one launch: counted for `path` and appended to the calling thread's
+// description of its current library call (M rows of x, grid, workgroup
+// size, dynamic LDS bytes).  Defined in qgemv_api.cpp.
+void note_launch(Path path, int M, int grid, int block, size_t lds);
+
 hipError_t launch_int4_gemv(const uint16_t* x, int64_t ldx, const uint8_t* w,
                             const uint16_t* scales, const uint8_t* zp, void* y,
                             int64_t ldy, int y_type, int M, int N, int K,

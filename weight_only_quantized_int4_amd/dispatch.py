@@ -1,0 +1,181 @@
+"""Decode-time dispatch on top of the C ABI: q4_K plane registration with
+liveness labels, and row groups for any number of rows of x.
+
+q4_K plane ("62 . r59 -- q4_K W_dsc plane + riders", section 3.1): the plane of
+a weight is built once at load time and kept in a map keyed by the weight's
+device pointer.  A call takes the plane when one is registered.  When a
+registration failed, the call degrades to in-kernel decode, with a warning
+once per process and a visible label: "a fast path that degrades correctly
+must carry a visible label", because parity cannot see the path.  Labels
+(counted by ``liveness()``):
+
+    dsc-plane             the plane was used
+    in-kernel(dsc=off)    no plane registered for this weight, or the plane
+                          path is switched off (QGEMV_Q4K_DSC=0, or
+                          use_plane=False) -- the page's contrast switch
+    in-kernel(fallback!)  a registration was attempted and failed
+
+Rows (the AstrAI backend commit list: decode-time linear layers go to the GEMV
+for small M): the kernels take M = 1..8; these wrappers take any M >= 1 and
+run row groups of at most 8 rows of x (each group reads the weights again).
+
+Everything here is argument handling; every output element is computed by the
+library's HIP kernels.  ``explain()`` returns the library's description of the
+kernels the calling thread's last call enqueued.
+"""
+from __future__ import annotations
+
+import os
+import threading
+import warnings
+from typing import Optional, Tuple
+
+import torch
+
+from . import qgemv as _q
+
+MAX_ROWS = 8
+LABEL_PLANE = "dsc-plane"
+LABEL_OFF = "in-kernel(dsc=off)"
+LABEL_FALLBACK = "in-kernel(fallback!)"
+
+_lock = threading.Lock()
+_planes = {}   # weight device pointer -> plane tensor
+_failed = {}   # weight device pointer -> reason the registration failed
+_warned = False
+_liveness = {LABEL_PLANE: 0, LABEL_OFF: 0, LABEL_FALLBACK: 0}
+
+
+def _plane_enabled() -> bool:
+    return os.environ.get("QGEMV_Q4K_DSC", "1") != "0"
+
+
+def q4k_shape(w: torch.Tensor) -> Tuple[int, int]:
+    """(N, K) of raw q4_K weights stored as uint8 [N, K/256*144]."""
+    if w.dim() != 2 or w.shape[1] % 144 != 0:
+        raise ValueError("q4_K weights must be a 2-D uint8 tensor [N, K/256*144]")
+    return w.shape[0], w.shape[1] // 144 * 256
+
+
+def register_q4k_plane(w: torch.Tensor, stream=None) -> bool:
+    """Build the W_dsc plane of raw q4_K weights ``w`` and register it under
+    w's device pointer.  Returns False, and remembers why, when the plane
+    cannot be allocated or built; calls on ``w`` then fall back to in-kernel
+    decode with the fallback label."""
+    key = w.data_ptr()
+    try:
+        N, K = q4k_shape(w)
+        nbytes = _q.q4k_dsc_plane_bytes(N, K)
+        if nbytes == 0 and N > 0:
+            raise ValueError(f"no plane for N={N}, K={K}")
+        dsc = torch.empty((nbytes // 8, 2), dtype=torch.float32, device=w.device)
+        _q.q4k_build_dsc_plane(w, dsc, N, K, stream)
+    except (ValueError, RuntimeError) as e:  # QgemvError and allocation failures included
+        with _lock:
+            _planes.pop(key, None)
+            _failed[key] = str(e)
+        return False
+    with _lock:
+        _planes[key] = dsc
+        _failed.pop(key, None)
+    return True
+
+
+def unregister_q4k_plane(w: torch.Tensor) -> None:
+    with _lock:
+        _planes.pop(w.data_ptr(), None)
+        _failed.pop(w.data_ptr(), None)
+
+
+def q4k_plane_of(w: torch.Tensor) -> Optional[torch.Tensor]:
+    with _lock:
+        return _planes.get(w.data_ptr())
+
+
+def _row_groups(M: int):
+    for m0 in range(0, M, MAX_ROWS):
+        yield m0, min(M, m0 + MAX_ROWS)
+
+
+def _count(label: str) -> None:
+    with _lock:
+        _liveness[label] += 1
+
+
+def q4k_linear(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = None,
+               use_plane: bool = True, stream=None) -> Tuple[torch.Tensor, str]:
+    """y[M, N] = x[M, K] . dequant(w)^T for raw q4_K weights, through the
+    registered plane when there is one.  Returns (y, liveness label)."""
+    global _warned
+    N, K = q4k_shape(w)
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    key = w.data_ptr()
+    with _lock:
+        dsc = _planes.get(key)
+        failure = _failed.get(key)
+    if not (use_plane and _plane_enabled()):
+        label, dsc = LABEL_OFF, None
+    elif dsc is not None:
+        label = LABEL_PLANE
+    elif failure is not None:
+        label = LABEL_FALLBACK
+        if not _warned:
+            _warned = True
+            warnings.warn(f"q4_K plane unavailable ({failure}); falling back to in-kernel "
+                          f"decode (this warning is shown once per process)", RuntimeWarning,
+                          stacklevel=2)
+    else:
+        label = LABEL_OFF
+    for m0, m1 in _row_groups(M):
+        if dsc is not None:
+            _q.qgemv_q4k_dsc(x[m0:m1], w, dsc, y[m0:m1], stream)
+        else:
+            _q.qgemv_q4k(x[m0:m1], w, y[m0:m1], stream)
+    _count(label)
+    return y, label
+
+
+def int4_linear(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
+                zero_points: Optional[torch.Tensor], block_size: int,
+                y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """MatMulNBits int4 for any M >= 1 (row groups of at most 8); fp16 y
+    unless ``y`` is given."""
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, w.shape[0]), dtype=torch.float16, device=x.device)
+    for m0, m1 in _row_groups(M):
+        _q.qgemv_int4_blockwise(x[m0:m1], w, scales, zero_points, y[m0:m1], block_size, stream)
+    return y
+
+
+def bf16_linear(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """bf16 GEMV for any M >= 1 (row groups of at most 8); bf16 y unless
+    ``y`` is given."""
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, w.shape[0]), dtype=torch.bfloat16, device=x.device)
+    for m0, m1 in _row_groups(M):
+        _q.gemv_bf16(x[m0:m1], w, y[m0:m1], stream)
+    return y
+
+
+def liveness() -> dict:
+    """Calls per q4_K liveness label since the last reset."""
+    with _lock:
+        return dict(_liveness)
+
+
+def reset_liveness() -> None:
+    global _warned
+    with _lock:
+        for k in _liveness:
+            _liveness[k] = 0
+    _warned = False
+
+
+def explain() -> str:
+    """The kernels the calling thread's last library call enqueued."""
+    return _q.last_launch()

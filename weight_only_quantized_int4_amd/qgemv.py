@@ -58,6 +58,10 @@ def load_library() -> ctypes.CDLL:
         "q4k_build_dsc_plane": (St, [P, P, I64, I64, P]),
         "qg_status_string": (ctypes.c_char_p, [St]),
         "qg_last_error": (ctypes.c_char_p, []),
+        "qg_last_launch": (ctypes.c_char_p, []),
+        "qg_path_count": (I32, []),
+        "qg_path_name": (ctypes.c_char_p, [I32]),
+        "qg_path_launches": (ctypes.c_uint64, [I32]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -143,3 +147,19 @@ def q4k_build_dsc_plane(w: torch.Tensor, dsc_out: torch.Tensor, N: int, K: int,
     _check("q4k_build_dsc_plane", load_library().q4k_build_dsc_plane(
         _ptr(w), _ptr(dsc_out), N, K, _stream(stream)))
     return dsc_out
+
+
+def last_launch() -> str:
+    """Kernels enqueued by this thread's last library call ("" if none)."""
+    return load_library().qg_last_launch().decode()
+
+
+def path_names() -> list:
+    L = load_library()
+    return [L.qg_path_name(i).decode() for i in range(L.qg_path_count())]
+
+
+def path_launches() -> dict:
+    """Launches per kernel path since the library was loaded (all threads)."""
+    L = load_library()
+    return {L.qg_path_name(i).decode(): int(L.qg_path_launches(i)) for i in range(L.qg_path_count())}
