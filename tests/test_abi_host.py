@@ -188,7 +188,7 @@ def test_product_package_does_not_import_the_oracle():
 def test_liveness_exports_on_the_host():
     # host-only functions: no GPU needed
     names = q.path_names()
-    assert len(names) == q.load_library().qg_path_count() == 13
+    assert len(names) == q.load_library().qg_path_count() == 14
     assert names[0] == "int4_dot2_persistent" and "q4k_persistent_plane" in names
     assert q.load_library().qg_path_name(-1) is None
     assert q.load_library().qg_path_name(len(names)) is None

@@ -114,6 +114,53 @@ def test_matrix_core_x_above_64k(N):
     assert_accept(got, yr[:M], S[:M], "f32", f"int4 large x N={N}")
 
 
+@pytest.mark.parametrize("N,K,bs,asym,M,sampled", [(4096, 11008, 32, False, 8, True),
+                                                  (4100, 11008, 64, True, 8, True),
+                                                  (1000, 16384, 128, True, 5, False),
+                                                  (520, 9856, 32, True, 8, False)])
+def test_matrix_core_x_in_chunks(N, K, bs, asym, M, sampled):
+    # x beyond the LDS left beside the split partials: the split kernel stages
+    # x in chunks (two here), one tile per workgroup.  9856 = 77 items: x fits
+    # whole (154 KB) but not with the partials.
+    say(f"int4 matrix-core chunked x N={N} K={K} bs={bs} asym={asym} M={M}")
+    p = int4_case(N, K, bs, asym, 80 + M)
+    y = y_host(_run(p, M, torch.float32))
+    assert "int4_mfma_phased" in q.last_launch(), q.last_launch()
+    cols = tuple(sorted(set(np.random.default_rng(6).integers(0, N, 300).tolist()) | {0, 15, 16, N - 1})) \
+        if sampled else None
+    yr, S = int4_ref(N, K, bs, asym, 80 + M, cols)
+    got = y if cols is None else y[:, list(cols)]
+    assert_accept(got, yr[:M], S[:M], "f32", f"int4 chunked x {N}x{K} M={M}")
+
+
+def test_one_hot_probe_chunked_x_is_bit_exact():
+    """M = 8, K = 11008 (x staged in two chunks): row r of x is one-hot at k_r,
+    positions spread over both chunks and their seams; y must equal the
+    oracle's dequantized weights bitwise."""
+    N, K, bs = 48, 11008, 64
+    p = int4_case(N, K, bs, True, 34)
+    wdq = oracle.int4_dequant(p.w, p.scales, p.zp, N, K, bs)
+    wd, sd, zd = to_dev(p.w), f16_dev(p.scales), to_dev(p.zp)
+    seam = 43 * 128  # first k of the second chunk
+    ks = sorted(set(list(range(0, K, 97)) + [seam - 2, seam - 1, seam, seam + 1, K - 1]))
+    say(f"int4 chunked one-hot probe K={K}: {len(ks)} positions")
+    for i0 in range(0, len(ks), 8):
+        kk = ks[i0:i0 + 8]
+        M = len(kk)
+        x = torch.zeros((M, K), dtype=torch.float16, device=DEV)
+        for r, k in enumerate(kk):
+            x[r, k] = 1.0
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        q.qgemv_int4_blockwise(x, wd, sd, zd, y, bs)
+        if M == 8:
+            assert "int4_mfma_phased" in q.last_launch(), q.last_launch()
+        got = y.cpu().numpy()
+        want = wdq[:, kk].T.astype(np.float32)
+        assert np.array_equal(got, want), kk
+        nz = want != 0
+        assert np.array_equal(got.view(np.uint32)[nz], want.view(np.uint32)[nz]), kk
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_lm_head_shape_sampled(M):
     N, K = 151936, 4096
@@ -249,6 +296,22 @@ def test_wide_matrix_sampled(bs, asym, M):
     cols = tuple(sorted(set(rng.integers(0, N, 500).tolist()) | {0, 15, 16, N - 1}))
     yr, S = int4_ref(N, K, bs, asym, 600 + bs, cols)
     assert_accept(y[:, list(cols)], yr[:M], S[:M], "f32", f"int4 wide bs={bs} M={M}")
+
+
+@pytest.mark.parametrize("N,K,bs,asym", [(4096, 11008, 32, False), (4100, 14336, 32, True),
+                                         (4096, 4096, 128, True), (11008, 4096, 128, False),
+                                         (6912, 1536, 64, True)])
+def test_layer_shapes_single_row_sampled(N, K, bs, asym):
+    # The single-row launch shapes of 7B-class layers: 512-thread workgroups
+    # for rows of 8192 weights or more, lanes per row widened for short N, and
+    # a ragged last tile (4100 rows).
+    say(f"int4 layer N={N} K={K} bs={bs} asym={asym} M=1")
+    p = int4_case(N, K, bs, asym, 700 + bs)
+    y = y_host(_run(p, 1, torch.float32))
+    rng = np.random.default_rng(5)
+    cols = tuple(sorted(set(rng.integers(0, N, 400).tolist()) | {0, 1, 63, 64, N - 2, N - 1}))
+    yr, S = int4_ref(N, K, bs, asym, 700 + bs, cols)
+    assert_accept(y[:, list(cols)], yr[:1], S[:1], "f32", f"int4 layer {N}x{K} bs={bs}")
 
 
 def test_misaligned_scales_and_zero_points():

@@ -239,14 +239,14 @@ struct Item {
   uint32_t z[R][PB];  // zero-point byte per piece
 };
 
-template <int M, int LPR, int R, int PB, bool ZP, bool STRIDED>
-__global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
+template <int M, int LPR, int R, int PB, bool ZP, bool STRIDED, int NT>
+__global__ __launch_bounds__(NT) void int4_gemv_persistent(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zp, int zrow,
     void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int bs_log2, int ntiles,
     int x_vec16) {
   extern __shared__ uint4 xs[];  // [M][K/32][5]: 4 permuted groups of 8 halves + pad
-  constexpr int S = kBlock / LPR;  // row slots per workgroup
+  constexpr int S = NT / LPR;  // row slots per workgroup
   constexpr int RT = S * R;        // rows per tile
   const int tid = threadIdx.x;
   const int slot = tid / LPR;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
   Item<R, PB> cur;
   const int groups = K >> 3;
   stage_slots<4>(
-      tid, kBlock, M * groups,
+      tid, NT, M * groups,
       [&](int t) {
         const int m = t / groups;
         return load_x8(x + m * ldx + (t - m * groups) * 8, x_vec16);
@@ -415,30 +415,50 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_persistent(
 // the A reads of rows 0..3 fall in distinct banks.  SPLIT: all NW waves of a
 // workgroup share one tile and split its items; the partial sums are added in
 // LDS in wave order (deterministic).  Otherwise each wave owns whole tiles.
+// PHASED (with SPLIT, one tile per workgroup): x is staged in chunks of `cp`
+// items when all of it does not fit in LDS; the waves split each chunk's
+// items, keep their accumulators across chunks, and the workgroup restages x
+// between chunks.
 // D needs no cross-lane reduction: lane (n, g) ends with rows 4g..4g+3 of
 // column n.
-template <int M, bool ZP, int PPB, bool SPLIT, int NW, int DG>
+// x slots each thread loads before it stores them (matrix-core kernel;
+// measured on the 4096-row 7B layers: 12 and 16 are slower).
+constexpr int kMfmaStageUnroll = 4;
+
+template <int M, bool ZP, int PPB, bool SPLIT, int NW, int DG, bool PHASED = false>
 __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zp, int zrow,
     void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int bs_log2, int ntiles,
-    int x_vec16) {
+    int x_vec16, int cp) {
+  static_assert(!PHASED || SPLIT, "chunks of x are staged per tile: split mode only");
   static_assert(PPB == 1 || PPB == 2 || PPB == 4, "pieces per scale block");
-  extern __shared__ uint4 xs[];  // [M][K/8] slots, swizzled; then the SPLIT partials
+  extern __shared__ uint4 xs[];  // [M][CP*16] slots, swizzled; then the SPLIT partials
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = lane & 15, g = lane >> 4;
-  const int S8 = K >> 3;  // 16-byte slots per x row
   const int nb = K >> bs_log2;
-  const int C = K >> 7;   // items per row
-  // This wave's stream of tiles (t0, t0 + TS, ...) and its item range per tile.
+  const int C = K >> 7;                                // items per row
+  const int CP = PHASED ? cp : C;                      // items per staged chunk of x
+  const int nph = PHASED ? (C + CP - 1) / CP : 1;      // chunks
+  const int S8 = CP << 4;                              // 16-byte slots per staged x row
+  // This wave's stream of tiles (t0, t0 + TS, ...) and its item range
+  // [item_begin(p), item_end(p)) in chunk p of each tile.
   const int t0 = SPLIT ? (int)blockIdx.x : (int)blockIdx.x * NW + wave;
   const int TS = SPLIT ? (int)gridDim.x : (int)gridDim.x * NW;
-  const int cb = SPLIT ? wave * C / NW : 0;
-  const int ce = SPLIT ? (wave + 1) * C / NW : C;
+  auto item_begin = [&](int p) {
+    const int base = p * CP, len = (C - base < CP ? C - base : CP);
+    return SPLIT ? base + wave * len / NW : base;
+  };
+  auto item_end = [&](int p) {
+    const int base = p * CP, len = (C - base < CP ? C - base : CP);
+    return SPLIT ? base + (wave + 1) * len / NW : base + len;
+  };
   const int my_tiles = t0 < ntiles ? (ntiles - t0 + TS - 1) / TS : 0;
-  const int ngroups = my_tiles * ((ce - cb + 3) >> 2);
+  int groups_per_tile = 0;
+  for (int p = 0; p < nph; ++p) groups_per_tile += (item_end(p) - item_begin(p) + 3) >> 2;
+  const int ngroups = my_tiles * groups_per_tile;
   const uint32_t magic = vreg_const(0x64006400u);
   // Slot swizzle of x row n: PPB = 4 reads slots 16c + 4g + t, the others
   // 16c + 4t + g; the swizzle flips the bits that t selects.
@@ -451,9 +471,15 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     SType s;     // scales of item gc+g
     uint32_t z;  // zero-point bytes of item gc+g (PPB 1: 2 bytes, else 1)
   };
+  // Position in the stream: tile, chunk, first item of the group, end of the
+  // wave's items in that chunk.
+  struct Cursor {
+    int tile, p, gc, e;
+  };
   const char* sbytes = reinterpret_cast<const char*>(scales);
-  auto issue = [&](Group& gr, int tile, int gc) {
-    const int row = tile * 16 + n;
+  auto issue = [&](Group& gr, const Cursor& cu) {
+    const int gc = cu.gc, ce = cu.e;
+    const int row = cu.tile * 16 + n;
     const uint32_t nl = (uint32_t)(row < N ? row : N - 1);
     const uint32_t wrow = nl * (uint32_t)(K >> 1);
 #pragma unroll
@@ -474,34 +500,45 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
       gr.z = 0x8888u;
     }
   };
-  auto advance = [&](int& tile, int& gc) {
-    gc += 4;
-    if (gc >= ce) {
-      gc = cb;
-      tile += TS;
+  auto advance = [&](Cursor& cu) {
+    cu.gc += 4;
+    if (cu.gc >= cu.e) {
+      if (++cu.p == nph) {
+        cu.p = 0;
+        cu.tile += TS;
+      }
+      cu.gc = item_begin(cu.p);
+      cu.e = item_end(cu.p);
     }
   };
 
+  // Chunk p of x: L8 slots of each row, from slot p * CP * 16 of the row.
+  auto stage_load = [&](int p, int L8, int t) {
+    const int m = t / L8;
+    return load_x8(x + m * ldx + (p * S8 + (t - m * L8)) * 8, x_vec16);
+  };
+  auto stage_store = [&](int L8, int t, uint4 v) {
+    const int m = t / L8;
+    const int gi = t - m * L8;
+    xs[m * S8 + (gi ^ ((m & 3) << kSwzShift))] = pair_halves(v);
+  };
+  auto chunk_slots = [&](int p) { return (C - p * CP < CP ? C - p * CP : CP) << 4; };
+
   Group ring[DG];
-  int lt = t0, lgc = cb;  // next group to load
-  stage_slots<4>(
-      tid, NW * kWave, M * S8,
-      [&](int t) {
-        const int m = t / S8;
-        return load_x8(x + m * ldx + (t - m * S8) * 8, x_vec16);
-      },
-      [&](int t, uint4 v) {
-        const int m = t / S8;
-        const int gi = t - m * S8;
-        xs[m * S8 + (gi ^ ((m & 3) << kSwzShift))] = pair_halves(v);
-      },
-      [&] {  // unconditional: rows past the end are clamped
+  Cursor lc = {t0, 0, item_begin(0), item_end(0)};  // next group to load
+  {
+    const int L8 = chunk_slots(0);
+    stage_slots<kMfmaStageUnroll>(
+        tid, NW * kWave, M * L8, [&](int t) { return stage_load(0, L8, t); },
+        [&](int t, uint4 v) { stage_store(L8, t, v); },
+        [&] {  // unconditional: rows past the end are clamped
 #pragma unroll
-        for (int k = 0; k < DG; ++k) {
-          issue(ring[k], lt, lgc);
-          advance(lt, lgc);
-        }
-      });
+          for (int k = 0; k < DG; ++k) {
+            issue(ring[k], lc);
+            advance(lc);
+          }
+        });
+  }
   __syncthreads();
 
   // LDS byte address of the A slot that MFMA t of item 0 reads (rows >= M
@@ -527,7 +564,8 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     out[0] = e01[0]; out[1] = e01[1]; out[2] = e23[0]; out[3] = e23[1];
   };
 
-  auto consume = [&](const Group& gr, int tile, int gc) {
+  auto consume = [&](const Group& gr, const Cursor& cu) {
+    const int tile = cu.tile, gc = cu.gc, ce = cu.e;
     // Scales and zero points of items gc..gc+3, in every lane.
     uint32_t s_lo[4], s_hi[4], zb[4];
     if constexpr (PPB == 1) {
@@ -541,7 +579,7 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     for (int j = 0; j < 4; ++j) {
       const int c = gc + j;
       if (c >= ce) break;  // partial last group of a tile (uniform)
-      const uint32_t ibase = (uint32_t)c * 256u;
+      const uint32_t ibase = (uint32_t)(c - cu.p * CP) * 256u;
       uint4 av[4];  // A operands of the item's 4 MFMAs
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -598,7 +636,15 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
           for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, d[i], acc[i]);
         }
       }
-      if (c == ce - 1) {  // tile finished: lane (n, g) holds rows 4g..4g+3 of column n
+      if (PHASED && c == ce - 1 && cu.p < nph - 1) {
+        // Chunk finished: once every wave is done with it, stage the next.
+        __syncthreads();
+        const int L8 = chunk_slots(cu.p + 1);
+        stage_slots<kMfmaStageUnroll>(
+            tid, NW * kWave, M * L8, [&](int t) { return stage_load(cu.p + 1, L8, t); },
+            [&](int t, uint4 v) { stage_store(L8, t, v); });
+        __syncthreads();
+      } else if (c == ce - 1) {  // tile finished: lane (n, g) holds rows 4g..4g+3 of column n
         const int row = tile * 16 + n;
         if constexpr (SPLIT) {
           f32x4* red = reinterpret_cast<f32x4*>(xs + M * S8);  // [NW][64]
@@ -634,23 +680,23 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     }
   };
 
-  int pt = t0, pgc = cb;  // next group to consume
+  Cursor pc = {t0, 0, item_begin(0), item_end(0)};  // next group to consume
   int u = 0;
 #pragma unroll 1
   for (; u + DG <= ngroups; u += DG) {
 #pragma unroll
     for (int k = 0; k < DG; ++k) {
-      consume(ring[k], pt, pgc);
-      advance(pt, pgc);
-      issue(ring[k], lt, lgc);
-      advance(lt, lgc);
+      consume(ring[k], pc);
+      advance(pc);
+      issue(ring[k], lc);
+      advance(lc);
     }
   }
 #pragma unroll
   for (int k = 0; k < DG; ++k) {
     if (u + k < ngroups) {
-      consume(ring[k], pt, pgc);
-      advance(pt, pgc);
+      consume(ring[k], pc);
+      advance(pc);
     }
   }
 }
@@ -661,32 +707,57 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
 constexpr bool kStrided = true;
 constexpr bool kBalanced = false;
 
+// Threads per workgroup of the persistent kernel at M = 1: 512 for long rows,
+// where staging x once per workgroup costs as much as a tile of weights
+// (measured: 4096 x 11008 and 4096 x 14336 gain a third; the 4096-wide
+// lm_head and 11008 x 4096 lose a few percent at 512), else 256.
+constexpr int kLongRowK = 8192;
+
+template <int M, int LPR, int R, int PB, int NT>
+hipError_t launch_persistent(const uint16_t* x, int64_t ldx, const uint8_t* w,
+                             const uint16_t* scales, const uint8_t* zp, void* y, int64_t ldy,
+                             int y_type, int N, int K, int block_size, size_t shmem,
+                             hipStream_t stream) {
+  constexpr int RT = (NT / LPR) * R;
+  const int bs_log2 = __builtin_ctz((unsigned)block_size);
+  const int zrow = ((K / block_size) + 1) / 2;
+  const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
+  const int ntiles = (N + RT - 1) / RT;
+  auto kern = zp ? int4_gemv_persistent<M, LPR, R, PB, true, kStrided, NT>
+                 : int4_gemv_persistent<M, LPR, R, PB, false, kStrided, NT>;
+  const int cap = resident_workgroups(kern, NT, shmem);
+  // Equal tile counts per workgroup: the fewest rounds that fit, then the
+  // smallest grid that still covers every tile in that many rounds.
+  const int rounds = (ntiles + cap - 1) / cap;
+  const int grid = kBalanced ? (ntiles + rounds - 1) / rounds : (ntiles < cap ? ntiles : cap);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), shmem, stream, x, ldx, w, scales, zp, zrow, y,
+                     ldy, y_type, N, K, bs_log2, ntiles, x_vec16);
+  note_launch(kPathInt4Dot2Persistent, M, grid, NT, shmem);
+  return hipGetLastError();
+}
+
 template <int M, int LPR, int R, int PB = 1>
 hipError_t launch_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* scales,
                       const uint8_t* zp, void* y, int64_t ldy, int y_type, int N, int K,
                       int block_size, hipStream_t stream) {
+  // x takes 80 bytes of LDS per 32 elements and row.
+  const size_t full = (size_t)M * (K / 32) * 80;
+  if constexpr (LPR <= kWave) {
+    if (full <= (size_t)kLdsBudget) {
+      if constexpr (M == 1) {
+        if (K >= kLongRowK)
+          return launch_persistent<M, LPR, R, PB, 512>(x, ldx, w, scales, zp, y, ldy, y_type, N,
+                                                      K, block_size, full, stream);
+      }
+      return launch_persistent<M, LPR, R, PB, kBlock>(x, ldx, w, scales, zp, y, ldy, y_type, N,
+                                                      K, block_size, full, stream);
+    }
+  }
   constexpr int RT = (kBlock / LPR) * R;
   const int bs_log2 = __builtin_ctz((unsigned)block_size);
   const int zrow = ((K / block_size) + 1) / 2;
   const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
   const int ntiles = (N + RT - 1) / RT;
-  // x takes 80 bytes of LDS per 32 elements and row.
-  const size_t full = (size_t)M * (K / 32) * 80;
-  if constexpr (LPR <= kWave) {
-   if (full <= (size_t)kLdsBudget) {
-    auto kern = zp ? int4_gemv_persistent<M, LPR, R, PB, true, kStrided>
-                   : int4_gemv_persistent<M, LPR, R, PB, false, kStrided>;
-    const int cap = resident_workgroups(kern, kBlock, full);
-    // Equal tile counts per workgroup: the fewest rounds that fit, then the
-    // smallest grid that still covers every tile in that many rounds.
-    const int rounds = (ntiles + cap - 1) / cap;
-    const int grid = kBalanced ? (ntiles + rounds - 1) / rounds : (ntiles < cap ? ntiles : cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), full, stream, x, ldx, w, scales, zp, zrow,
-                       y, ldy, y_type, N, K, bs_log2, ntiles, x_vec16);
-    note_launch(kPathInt4Dot2Persistent, M, grid, kBlock, full);
-    return hipGetLastError();
-   }
-  }
   const int grid = ntiles;
   int KC = (kLdsXBudget / (80 * M)) * 32;
   if (KC > K) KC = K;
@@ -710,52 +781,88 @@ constexpr int kMfmaMinM = 2;
 // items) in flight per lane.
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaDepth = 1;
+// The same for the split kernel (the waves of a workgroup share each tile;
+// measured on the 4096-row 7B layers: 16 waves, or 2 to 4 groups in flight,
+// are slower).
+constexpr int kSplitWaves = 8;
+constexpr int kSplitDepth = 1;
 
-template <int M, int PPB, bool SPLIT>
+template <int M, int PPB, bool SPLIT, bool PHASED = false>
 hipError_t launch_mfma_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w,
                            const uint16_t* scales, const uint8_t* zp, void* y, int64_t ldy,
-                           int y_type, int N, int K, int block_size, size_t shmem,
+                           int y_type, int N, int K, int block_size, size_t shmem, int cp,
                            hipStream_t stream) {
-  constexpr int NW = kMfmaWaves;
+  constexpr int NW = SPLIT ? kSplitWaves : kMfmaWaves;
+  constexpr int DG = SPLIT ? kSplitDepth : kMfmaDepth;
   const int bs_log2 = __builtin_ctz((unsigned)block_size);
   const int zrow = ((K / block_size) + 1) / 2;
   const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
   const int ntiles = (N + 15) / 16;
-  auto kern = zp ? int4_gemv_mfma<M, true, PPB, SPLIT, NW, kMfmaDepth>
-                 : int4_gemv_mfma<M, false, PPB, SPLIT, NW, kMfmaDepth>;
+  auto kern = zp ? int4_gemv_mfma<M, true, PPB, SPLIT, NW, DG, PHASED>
+                 : int4_gemv_mfma<M, false, PPB, SPLIT, NW, DG, PHASED>;
   const hipError_t e = allow_lds(kern, shmem);
   if (e != hipSuccess) return e;
-  const int cap = resident_workgroups(kern, NW * kWave, shmem);
+  // Phased: one tile per workgroup (the chunks of x are staged per tile).
+  const int cap = PHASED ? ntiles : resident_workgroups(kern, NW * kWave, shmem);
   const int want = SPLIT ? ntiles : (ntiles + NW - 1) / NW;
   const int grid = want < cap ? want : cap;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * kWave), shmem, stream, x, ldx, w, scales, zp,
-                     zrow, y, ldy, y_type, N, K, bs_log2, ntiles, x_vec16);
-  note_launch(SPLIT ? kPathInt4MfmaSplit : kPathInt4MfmaTiles, M, grid, NW * kWave, shmem);
+                     zrow, y, ldy, y_type, N, K, bs_log2, ntiles, x_vec16, cp);
+  note_launch(PHASED ? kPathInt4MfmaPhased : SPLIT ? kPathInt4MfmaSplit : kPathInt4MfmaTiles, M,
+              grid, NW * kWave, shmem);
   return hipGetLastError();
+}
+
+// Chunks of x for the phased matrix-core kernel: the fewest chunks of equal
+// item counts (the last one shorter) whose x fits in LDS beside the split
+// partials.  Returns the items per chunk, or 0 when a chunk would leave some
+// wave without an item.
+inline int mfma_chunk_items(int M, int K) {
+  constexpr int NW = kSplitWaves;
+  const int C = K / 128;
+  const int64_t room = (int64_t)kLdsMax - (int64_t)NW * kWave * 16;
+  const int fit = (int)(room / ((int64_t)M * 256));
+  if (fit < NW) return 0;
+  const int nph = (C + fit - 1) / fit;
+  const int cp = (C + nph - 1) / nph;
+  return C - (nph - 1) * cp >= NW ? cp : 0;
 }
 
 // Whole tiles per wave when the tiles fill at least half of the resident
 // wavefront slots; otherwise (and when every wave gets at least one item and
 // the partial sums fit in LDS) the waves of a workgroup split each tile.
+// When x itself does not fit in LDS, the split kernel stages it in chunks.
 template <int M, int PPB>
 hipError_t launch_mfma_ppb(const uint16_t* x, int64_t ldx, const uint8_t* w,
                            const uint16_t* scales, const uint8_t* zp, void* y, int64_t ldy,
                            int y_type, int N, int K, int block_size, hipStream_t stream) {
   constexpr int NW = kMfmaWaves;
   const size_t xbytes = (size_t)M * K * 2;
-  const size_t split_bytes = xbytes + (size_t)NW * kWave * 16;
+  const size_t partials = (size_t)kSplitWaves * kWave * 16;
+  const size_t split_bytes = xbytes + partials;
   const int ntiles = (N + 15) / 16;
-  if (K / 128 >= NW && split_bytes <= (size_t)kLdsMax) {
+  const bool x_fits = xbytes <= (size_t)kLdsMax;
+  int64_t waves = 0;
+  if (x_fits) {
     auto whole = int4_gemv_mfma<M, true, PPB, false, NW, kMfmaDepth>;
     const hipError_t e = allow_lds(whole, xbytes);
     if (e != hipSuccess) return e;
-    const int64_t waves = (int64_t)resident_workgroups(whole, NW * kWave, xbytes) * NW;
-    if (2LL * ntiles < waves)
-      return launch_mfma_cfg<M, PPB, true>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
-                                           block_size, split_bytes, stream);
+    waves = (int64_t)resident_workgroups(whole, NW * kWave, xbytes) * NW;
   }
+  const bool few_tiles = !x_fits || 2LL * ntiles < waves;
+  if (few_tiles && K / 128 >= kSplitWaves) {
+    if (split_bytes <= (size_t)kLdsMax)
+      return launch_mfma_cfg<M, PPB, true>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
+                                           block_size, split_bytes, K / 128, stream);
+    const int cp = mfma_chunk_items(M, K);
+    if (cp != 0)
+      return launch_mfma_cfg<M, PPB, true, true>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
+                                                 block_size, (size_t)M * cp * 256 + partials, cp,
+                                                 stream);
+  }
+  if (!x_fits) return hipErrorInvalidValue;  // launch_m checks this first
   return launch_mfma_cfg<M, PPB, false>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size,
-                                        xbytes, stream);
+                                        xbytes, K / 128, stream);
 }
 
 template <int M>
@@ -780,13 +887,16 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
     const uintptr_t salign = block_size >= 128 ? 2 : (size_t)8 * 32 / block_size;
     const bool aligned = (reinterpret_cast<uintptr_t>(scales) % salign == 0) &&
                          (block_size != 32 || reinterpret_cast<uintptr_t>(zp) % 2 == 0);
-    if (K % 128 == 0 && (size_t)M * K * 2 <= (size_t)kLdsMax && aligned)
+    if (K % 128 == 0 && aligned &&
+        ((size_t)M * K * 2 <= (size_t)kLdsMax || mfma_chunk_items(M, K) != 0))
       return launch_mfma<M>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
   }
   // Lanes per row (measured on the 151936 x 4096 lm_head shape): 32 is best at
   // small M, 8 at large M (more rows share each x read).  Take the first
   // preference that divides the row's piece count, so no lane idles in the
-  // last stride of a row; then widen it for short matrices.
+  // last stride of a row; then widen it for short matrices, up to twice the
+  // lanes of one full round of wavefronts (measured on the 4096-row layers of
+  // a 7B model: 4096 x 4096, 4096 x 11008, 4096 x 14336).
   const int P = K / 32;  // 16-byte pieces per row
   constexpr int pref[3] = {M <= 2 ? 32 : 8, 16, M <= 2 ? 8 : 32};
   int lpr = pref[0];
@@ -795,7 +905,7 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
       lpr = c;
       break;
     }
-  lpr = widen_lanes_per_row(lpr, N, P);
+  lpr = widen_lanes_per_row(lpr, N, P, 2 * kLanesToFill, true);
 #define QG_LAUNCH(L, RR) \
   return launch_cfg<M, L, RR>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream)
   switch (lpr) {

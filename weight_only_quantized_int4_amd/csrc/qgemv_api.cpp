@@ -27,10 +27,10 @@ thread_local char g_last_launch[512];
 thread_local int g_last_launch_count;
 
 const char* const kPathNames[qg::kPathCount] = {
-    "int4_dot2_persistent", "int4_dot2_tiled",   "int4_mfma_tiles",    "int4_mfma_split",
-    "q4k_persistent",       "q4k_persistent_plane", "q4k_tiled",       "q4k_tiled_plane",
-    "q4k_plane_build",      "bf16_aligned",      "bf16_mfma_tiles",    "bf16_mfma_split",
-    "bf16_general"};
+    "int4_dot2_persistent", "int4_dot2_tiled",      "int4_mfma_tiles", "int4_mfma_split",
+    "int4_mfma_phased",     "q4k_persistent",       "q4k_persistent_plane", "q4k_tiled",
+    "q4k_tiled_plane",      "q4k_plane_build",      "bf16_aligned",    "bf16_mfma_tiles",
+    "bf16_mfma_split",      "bf16_general"};
 
 void begin_call() {
   g_last_launch[0] = '\0';

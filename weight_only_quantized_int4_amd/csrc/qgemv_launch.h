@@ -17,6 +17,7 @@ enum Path : int {
   kPathInt4Dot2Tiled,
   kPathInt4MfmaTiles,
   kPathInt4MfmaSplit,
+  kPathInt4MfmaPhased,
   kPathQ4kPersistent,
   kPathQ4kPersistentPlane,
   kPathQ4kTiled,
@@ -63,10 +64,14 @@ constexpr int kLdsXBudget = kLdsBudget - 1024;
 constexpr int64_t kLanesToFill = 256LL * 8 * 64;
 
 // Lanes per row: start from `lpr` and double it (up to 256, and not past the
-// row's piece count) until the N rows occupy kLanesToFill lanes, so that
-// short, wide matrices still launch enough wavefronts to hide HBM latency.
-inline int widen_lanes_per_row(int lpr, int N, int pieces) {
-  while ((int64_t)N * lpr < kLanesToFill && lpr < 256 && lpr < pieces) lpr *= 2;
+// row's piece count) until the N rows occupy `fill` lanes, so that short,
+// wide matrices still launch enough wavefronts to hide HBM latency.  With
+// `whole_strides` a doubling must also leave no lane without a piece.
+inline int widen_lanes_per_row(int lpr, int N, int pieces, int64_t fill = kLanesToFill,
+                               bool whole_strides = false) {
+  while ((int64_t)N * lpr < fill && lpr < 256 &&
+         (whole_strides ? 2 * lpr <= pieces : lpr < pieces))
+    lpr *= 2;
   return lpr;
 }
 
