@@ -15,6 +15,10 @@ What it computes (see the header of ``qgemv_oracle.c`` for the sources):
 * ``q4k_build_plane`` / ``q4k_plane_gemv`` -- the chunk-major float2 plane
   (same page, sections 2.2 and 2.3).
 * ``bf16_gemv``  -- the dense bf16 GEMV (AstrAI backend commit list).
+* ``q8_quantize`` / ``q4k_mmq`` -- q4_K prefill with 8-bit activations: the
+  activation prepass and the per-chunk rank-1 rescale of exact integer dot
+  products ("62 . r59 -- q4_K W_dsc plane + riders", sections 2.1 and 3.2;
+  the activation rule is a reading, stated in ``qgemv_oracle.c``).
 
 Each GEMV returns ``(y_ref, S)`` in float64: ``y_ref = sum_k x*w`` and
 ``S = sum_k |x*w|``.  ``accept`` applies the rule
@@ -41,12 +45,18 @@ _LIB_OVERRIDE = os.environ.get("QGEMV_ORACLE_LIB")
 
 # Relative tolerance of the acceptance rule (fp32 accumulate, 16-bit output).
 RTOL = 2e-3
+# Relative tolerance of the q4_K x q8 product against its exact value: the
+# integer sums are exact, and fp32 evaluation of d_a*(dv*D + mv*Sa) plus the
+# running sum over K/32 chunks rounds at most K/32 + 4 times, each time by at
+# most 2^-24 of a partial magnitude bounded by S; (K/32 + 4) * 2^-24 < 1e-4 for
+# K <= 52000.
+RTOL_MMQ = 1e-4
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no contraction of a*b+c into an FMA)."""
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+        tmp = f"{_LIB}.{os.getpid()}.tmp"  # concurrent builders never share a file
         subprocess.check_call(
             ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
              "-Wall", "-Wextra", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
@@ -94,6 +104,9 @@ def lib() -> ctypes.CDLL:
             "oracle_q4k_gemv": (None, [P, I64, P, I64, I64, I64, P, I64, P, P]),
             "oracle_q4k_plane_gemv": (None, [P, I64, P, P, I64, I64, I64, P, I64, P, P]),
             "oracle_bf16_gemv": (None, [P, I64, P, I64, I64, I64, I64, P, I64, P, P]),
+            "oracle_q8_quantize_block": (None, [P, P, P]),
+            "oracle_q8_quantize_rows": (None, [P, I64, I64, I64, P, P]),
+            "oracle_q4k_mmq": (None, [P, I64, P, I64, I64, I64, P, I64, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -232,6 +245,36 @@ def q4k_plane_gemv(x: np.ndarray, w: np.ndarray, plane: np.ndarray, M: int, N: i
     s = np.zeros((M, nc), dtype=np.float64)
     lib().oracle_q4k_plane_gemv(_ptr(x), ldx, _ptr(w), _ptr(plane), M, N, K, _ptr(c),
                                 nc, y.ctypes.data, s.ctypes.data)
+    return y, s
+
+
+# ---------------------------------------------------------------------------
+# q4_K x 8-bit activations (prefill)
+# ---------------------------------------------------------------------------
+
+def q8_quantize(x: np.ndarray, T: int, K: int, ldx: Optional[int] = None):
+    """Codes int8 [T][K] and scales float32 [T][K/32] of x float32 [T][ldx]."""
+    ldx = K if ldx is None else ldx
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    q = np.zeros((T, K), dtype=np.int8)
+    d = np.zeros((T, K // 32), dtype=np.float32)
+    lib().oracle_q8_quantize_rows(_ptr(x), ldx, T, K, q.ctypes.data, d.ctypes.data)
+    return q, d
+
+
+def q4k_mmq(x: np.ndarray, w: np.ndarray, T: int, N: int, K: int,
+            cols: Optional[Sequence[int]] = None, ldx: Optional[int] = None):
+    """(y_ref, S) [T][ncols] of the q4_K x q8 product (see qgemv_oracle.c)."""
+    c, nc = _cols(cols, N)
+    ldx = K if ldx is None else ldx
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    qa = np.zeros((T, K), dtype=np.int8)
+    da = np.zeros((T, K // 32), dtype=np.float32)
+    qw = np.zeros(K, dtype=np.intc)
+    y = np.zeros((T, nc), dtype=np.float64)
+    s = np.zeros((T, nc), dtype=np.float64)
+    lib().oracle_q4k_mmq(_ptr(x), ldx, _ptr(w), T, N, K, _ptr(c), nc, qa.ctypes.data,
+                         da.ctypes.data, qw.ctypes.data, y.ctypes.data, s.ctypes.data)
     return y, s
 
 

@@ -102,3 +102,28 @@ def x_f16(bits: np.ndarray) -> np.ndarray:
 
 def x_bf16(bits: np.ndarray) -> np.ndarray:
     return _bf16(bits)
+
+
+def q8_quantize(x: np.ndarray, K: int):
+    """Per 32-block symmetric 8-bit codes of float32 rows x [T][K]: the scale
+    is amax/127 and the code x/scale rounded half away from zero, both
+    quotients in float32 (NumPy's float32 division is IEEE)."""
+    xb = np.asarray(x, dtype=np.float32).reshape(x.shape[0], K // 32, 32)
+    amax = np.abs(xb).max(axis=2)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(d == 0, np.float32(1.0), d).astype(np.float32)
+    v = (xb / safe[..., None]).astype(np.float32).astype(np.float64)
+    q = np.sign(v) * np.floor(np.abs(v) + 0.5)
+    q = np.where(d[..., None] == 0, 0.0, q)
+    return q.reshape(x.shape[0], K).astype(np.int64), d
+
+
+def q4k_mmq(x: np.ndarray, w: np.ndarray, N: int, K: int):
+    """The q4_K x q8 product: the GEMV of the dequantized activations
+    d_a * q_a with the exact weights dv * q + mv."""
+    q, d = q8_quantize(x, K)
+    xa = q.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+    dv, mv = q4k_coeffs(w, N, K)
+    wex = (np.repeat(dv.astype(np.float64), 32, axis=1) * q4k_codes(w, N, K)
+           + np.repeat(mv.astype(np.float64), 32, axis=1))
+    return xa @ wex.T

@@ -38,6 +38,19 @@
  *    multiply, exact negation).
  *  - bf16 dense GEMV: the AstrAI backend commit list (bf16 GEMV primitive for
  *    M = 1..8, any positive K and any storage offset).
+ *  - q4_K prefill with 8-bit activations (MMQ): "62 . r59 -- q4_K W_dsc plane
+ *    + riders", section 2.1 (the rank-1 rescale of each (chunk, row) integer
+ *    dot product by d*sc and -dmin*m) and section 3.2 (the dispatch arm
+ *    quantizes the activations to 8 bits in a prepass before the integer
+ *    matrix product).  The page does not spell out the activation rule; the
+ *    reading used here is the plain symmetric one, per block of 32
+ *    consecutive k of one activation row (one weight chunk, so one activation
+ *    scale multiplies each chunk's integer sum): d = amax/127 in binary32,
+ *    q = x/d in binary32 rounded half away from zero, d = 0 and q = 0 for an
+ *    all-zero block.  The result is the exact value of
+ *        sum_c d_a[c] * (dv[c] * sum_{k in c} q_w[k]*q_a[k]
+ *                        + mv[c] * sum_{k in c} q_a[k])
+ *    evaluated in double.
  */
 #include <math.h>
 #include <stddef.h>
@@ -426,4 +439,86 @@ void oracle_bf16_gemv(const uint16_t *x, int64_t ldx, const uint16_t *w,
     weights_t W = {ORACLE_W_BF16, (const uint8_t *)w, NULL, NULL, NULL, 0, ldw,
                    N, K};
     gemv(x, ORACLE_X_BF16, ldx, &W, M, cols, cols ? ncols : N, y_ref, s_abs);
+}
+
+/* ------------------------------------------------------------------------ */
+/* q4_K prefill with 8-bit activations.                                      */
+/* ------------------------------------------------------------------------ */
+
+/* One block of 32 activations -> 32 signed 8-bit codes and the block scale
+ * (see the file header for the rule).  Every operation is a single binary32
+ * operation: the division amax / 127, the division x / d, and the rounding of
+ * the quotient half away from zero to an integer (|x / d| <= 127 up to a few
+ * binary32 ulps, so the code fits in 8 bits). */
+void oracle_q8_quantize_block(const float *x, int8_t *q, float *d_out)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < 32; i++) {
+        float a = fabsf(x[i]);
+        if (a > amax)
+            amax = a;
+    }
+    float d = amax / 127.0f;
+    *d_out = d;
+    for (int i = 0; i < 32; i++) {
+        if (d == 0.0f) {
+            q[i] = 0;
+        } else {
+            float v = x[i] / d;
+            q[i] = (int8_t)roundf(v);
+        }
+    }
+}
+
+/* Rows of x[T][ldx] (K a multiple of 32) -> codes q[T][K] and scales
+ * d[T][K/32]. */
+void oracle_q8_quantize_rows(const float *x, int64_t ldx, int64_t T, int64_t K,
+                             int8_t *q, float *d)
+{
+    for (int64_t t = 0; t < T; t++)
+        for (int64_t b = 0; b < K / 32; b++)
+            oracle_q8_quantize_block(x + t * ldx + 32 * b, q + t * K + 32 * b,
+                                     d + t * (K / 32) + b);
+}
+
+/* y_ref[t, j] for every activation row t < T and listed weight row n =
+ * cols[j] (all N when cols is NULL): the sum over chunks c of
+ *     d_a[t,c] * (dv[n,c] * D + mv[n,c] * Sa)
+ * with the exact integers D = sum_{k in c} q_w[n,k] * q_a[t,k] and
+ * Sa = sum_{k in c} q_a[t,k]; S[t, j] sums the magnitudes of the two terms.
+ * The coefficients come from the super-block (oracle_q4k_coeffs) and the
+ * quants in GGUF order (oracle_q4k_code).  Outputs are [T][ncols]. */
+void oracle_q4k_mmq(const float *x, int64_t ldx, const uint8_t *w, int64_t T,
+                    int64_t N, int64_t K, const int64_t *cols, int64_t ncols,
+                    int8_t *qa, float *da, int *qw, double *y_ref,
+                    double *s_abs)
+{
+    /* qa [T][K], da [T][K/32] and qw [K] are caller-provided scratch. */
+    int64_t nchunk = K / 32;
+    int64_t nc = cols ? ncols : N;
+    oracle_q8_quantize_rows(x, ldx, T, K, qa, da);
+    for (int64_t j = 0; j < nc; j++) {
+        int64_t n = cols ? cols[j] : j;
+        for (int64_t k = 0; k < K; k++)
+            qw[k] = oracle_q4k_code(w, K, n, k);
+        for (int64_t t = 0; t < T; t++) {
+            double acc = 0.0, acc_abs = 0.0;
+            for (int64_t c = 0; c < nchunk; c++) {
+                float dv, mv;
+                oracle_q4k_coeffs(w, K, n, c, &dv, &mv); /* chunk c of row n */
+                int64_t dot = 0, sum = 0;
+                for (int64_t k = 32 * c; k < 32 * c + 32; k++) {
+                    dot += (int64_t)qw[k] * (int64_t)qa[t * K + k];
+                    sum += (int64_t)qa[t * K + k];
+                }
+                double a = (double)da[t * nchunk + c];
+                double term_d = a * ((double)dv * (double)dot);
+                double term_m = a * ((double)mv * (double)sum);
+                acc += term_d + term_m;
+                acc_abs += fabs(term_d) + fabs(term_m);
+            }
+            y_ref[t * nc + j] = acc;
+            s_abs[t * nc + j] = acc_abs;
+        }
+    }
 }

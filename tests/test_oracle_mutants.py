@@ -38,6 +38,16 @@ MUTANTS = {
                         "return oracle_bf16_to_f64(((const uint16_t *)W->w)[n * W->K + k]);"),
     "last k dropped": ("for (int64_t k = 0; k < W->K; k++) {", "for (int64_t k = 0; k < W->K - 1; k++) {"),
     "abs sum sign": ("acc_abs += fabs(p);", "acc_abs += p;"),
+    "q8 rounding half to even": ("q[i] = (int8_t)roundf(v);", "q[i] = (int8_t)rintf(v);"),
+    "q8 scale over 128": ("float d = amax / 127.0f;", "float d = amax / 128.0f;"),
+    "q8 signed maximum": ("float a = fabsf(x[i]);", "float a = x[i];"),
+    "mmq min term dropped": ("double term_m = a * ((double)mv * (double)sum);", "double term_m = 0.0;"),
+    "mmq activation scale missing on the min term": ("double term_m = a * ((double)mv * (double)sum);",
+                                                     "double term_m = (double)mv * (double)sum;"),
+    "mmq chunk coefficients": ("oracle_q4k_coeffs(w, K, n, c, &dv, &mv); /* chunk c of row n */",
+                               "oracle_q4k_coeffs(w, K, n, c / 2, &dv, &mv);"),
+    "mmq activation index": ("dot += (int64_t)qw[k] * (int64_t)qa[t * K + k];",
+                             "dot += (int64_t)qw[k] * (int64_t)qa[k];"),
 }
 
 

@@ -425,6 +425,137 @@ def test_bf16_against_numpy_cross_oracle(oracle_lib):
 
 
 # ---------------------------------------------------------------------------
+# q4_K x 8-bit activations (prefill)
+# ---------------------------------------------------------------------------
+
+def test_q8_worked_example(oracle_lib):
+    g = _gold("q8_worked_example.json")
+    for blk in g["blocks"]:
+        x = np.array(blk["x"], dtype=np.float32).reshape(1, 32)
+        q, d = oracle.q8_quantize(x, 1, 32)
+        assert float(d[0, 0]) == blk["d"]
+        assert q[0].tolist() == blk["q"]
+
+
+def _q8_blocks(rng, T, K):
+    """Rows of varied magnitude, with exact halfway quotients planted."""
+    x = (rng.standard_normal((T, K)) * rng.uniform(1e-3, 50.0, (T, 1))).astype(np.float32)
+    xb = x.reshape(T, K // 32, 32)
+    # block 0 of every row: amax 127/16 (scale exactly 1/16) and halfway codes
+    xb[:, 0, :] = (rng.integers(-126, 126, (T, 32)) + 0.5 * rng.integers(0, 2, (T, 32))) / 16.0
+    xb[:, 0, 0] = -127 / 16.0
+    xb[:, 1, :] = 0.0  # an all-zero block
+    return np.ascontiguousarray(xb.reshape(T, K))
+
+
+def test_q8_invariants(oracle_lib):
+    rng = np.random.default_rng(21)
+    T, K = 6, 512
+    x = _q8_blocks(rng, T, K)
+    q, d = oracle.q8_quantize(x, T, K)
+    xb = x.reshape(T, K // 32, 32).astype(np.float64)
+    qb = q.reshape(T, K // 32, 32).astype(np.int64)
+    amax = np.abs(xb).max(axis=2)
+    assert np.all(np.abs(qb) <= 127)
+    # the scale is the binary32 quotient amax / 127
+    assert np.array_equal(d, (amax.astype(np.float32) / np.float32(127.0)).astype(np.float32))
+    dd = d.astype(np.float64)[..., None]
+    # the largest magnitude maps to +-127, signs agree, error within half a step
+    arg = np.abs(xb).argmax(axis=2)
+    at = np.take_along_axis(qb, arg[..., None], axis=2)[..., 0]
+    xat = np.take_along_axis(xb, arg[..., None], axis=2)[..., 0]
+    nz = amax > 0
+    assert np.all(at[nz] == np.where(xat[nz] > 0, 127, -127))
+    assert np.all((qb == 0) | (np.sign(qb) == np.sign(xb)))
+    assert np.all(np.abs(xb - dd * qb) <= dd * (0.5 + 1e-5))
+    assert np.all(qb[~nz] == 0) and np.all(d[~nz] == 0)
+    # block 0: scale exactly 1/16, halfway quotients rounded away from zero
+    assert np.all(d[:, 0] == 0.0625)
+    v = xb[:, 0, :] * 16.0
+    assert np.array_equal(qb[:, 0, :], (np.sign(v) * np.floor(np.abs(v) + 0.5)).astype(np.int64))
+
+
+def test_q8_against_numpy_cross_oracle(oracle_lib):
+    rng = np.random.default_rng(22)
+    T, K = 9, 1024
+    x = _q8_blocks(rng, T, K)
+    q, d = oracle.q8_quantize(x, T, K)
+    qn, dn = npx.q8_quantize(x, K)
+    assert np.array_equal(q.astype(np.int64), qn) and np.array_equal(d.view(np.uint32), dn.view(np.uint32))
+
+
+def test_q4k_mmq_worked_example(oracle_lib):
+    g = _gold("q4k_mmq_worked_example.json")
+    w = _one_block(g["d_bits"], g["dmin_bits"], g["scale_bytes"], bytes([g["quant_byte"]]) * 128)
+    x = np.zeros((2, 256), dtype=np.float32)
+    for c in range(8):
+        x[0, 32 * c] = 127.0
+        x[0, 32 * c + 1] = c + 1
+    x[1] = x[0] * 0.5
+    y, S = oracle.q4k_mmq(x, w, 2, 1, 256)
+    assert y[:, 0].tolist() == g["y"] and S[:, 0].tolist() == g["S"]
+
+
+@pytest.mark.parametrize("N,K", [(2, 256), (3, 512)])
+def test_q4k_mmq_bruteforce_integer(oracle_lib, N, K):
+    """d = dmin = 1 and activation blocks with amax 127: d_a = 1, q_a = x and
+    w = s*q - m, so y is an exact integer matmul."""
+    rng = np.random.default_rng(30 + K + N)
+    nsb = K // 256
+    blocks = [_one_block(0x3C00, 0x3C00, rng.integers(0, 256, 12, dtype=np.uint8).tobytes(),
+                         rng.integers(0, 256, 128, dtype=np.uint8).tobytes()) for _ in range(N * nsb)]
+    w = np.concatenate(blocks).reshape(N, nsb * 144)
+    T = 4
+    x_int = rng.integers(-127, 128, (T, K))
+    x_int.reshape(T, K // 32, 32)[:, :, 5] = 127 * rng.choice([-1, 1], (T, K // 32))
+    x = x_int.astype(np.float32)
+    wint = []
+    for n in range(N):
+        row = []
+        for k in range(K):
+            sb, e = divmod(k, 256)
+            cc, l = divmod(e, 32)
+            sc = [int(v) for v in w[n, sb * 144 + 4:sb * 144 + 16]]
+            s_, m_ = oracle.q4k_scale_min(bytes(sc), cc)
+            byte = int(w[n, sb * 144 + 16 + 32 * (cc // 2) + l])
+            q_ = byte & 15 if cc % 2 == 0 else byte >> 4
+            row.append(s_ * q_ - m_)
+        wint.append(row)
+    want = _exact_int_matmul(x_int.tolist(), wint)
+    y, _ = oracle.q4k_mmq(x, w, T, N, K)
+    assert y.tolist() == [[float(v) for v in r] for r in want]
+
+
+def test_q4k_mmq_within_quantization_error_of_exact_gemv(oracle_lib):
+    """|y_mmq - x . w| is bounded by sum_k |w_k| * |x_k - d_a q_a,k|, the error
+    the 8-bit activations introduce (w exact in these distributions)."""
+    import datagen
+    N, K, T = 6, 1024, 3
+    p = datagen.q4k_problem(N, K, seed=31)
+    x = p.x[:T].copy()
+    y, S = oracle.q4k_mmq(x, p.w, T, N, K)
+    yg, _ = oracle.q4k_gemv(x, p.w, T, N, K)
+    q, d = oracle.q8_quantize(x, T, K)
+    dx = np.abs(x.astype(np.float64) - q * np.repeat(d.astype(np.float64), 32, axis=1))
+    wdq = np.abs(oracle.q4k_dequant(p.w, N, K))
+    bound = dx @ wdq.T
+    assert np.all(np.abs(y - yg) <= bound * (1 + 1e-9) + 1e-12 * S)
+    assert np.all(bound <= 0.02 * np.abs(x.astype(np.float64)) @ wdq.T)  # the bound is small
+
+
+@pytest.mark.parametrize("N,K,T", [(3, 256, 2), (5, 768, 4)])
+def test_q4k_mmq_against_numpy_cross_oracle(oracle_lib, N, K, T):
+    import datagen
+    p = datagen.q4k_problem(N, K, seed=32 + K)
+    x = p.x[:T].copy()
+    y, S = oracle.q4k_mmq(x, p.w, T, N, K)
+    yn = npx.q4k_mmq(x, p.w, N, K)
+    assert np.allclose(y, yn, rtol=1e-12, atol=1e-12 * float(np.abs(S).max()))
+    yc, Sc = oracle.q4k_mmq(x, p.w, T, N, K, cols=[N - 1, 0])
+    assert np.array_equal(yc, y[:, [N - 1, 0]]) and np.array_equal(Sc, S[:, [N - 1, 0]])
+
+
+# ---------------------------------------------------------------------------
 # the acceptance rule
 # ---------------------------------------------------------------------------
 
