@@ -21,6 +21,11 @@ Distributions (one per workload, as the decode workloads are specified):
 
 Draw order within one seed: weights, then scales, then zero points, then x.
 x is always drawn as 8 rows so that the M = 1..8 sweeps share a prefix.
+
+Prefill activations (the q4_K x 8-bit path): ``prefill_x`` draws T rows of
+x ~ N(0,1) in float32 from a seed of their own, with the row scale varying
+by a factor of 100 across rows (prompt tokens differ in magnitude) and one
+all-zero 32-block per row so that the zero-scale case is always present.
 """
 from __future__ import annotations
 
@@ -112,3 +117,15 @@ def q4k_header(d_bits: int, dmin_bits: int, sc12: bytes, qs128: bytes) -> bytes:
     assert len(sc12) == 12 and len(qs128) == 128
     return (int(d_bits).to_bytes(2, "little") + int(dmin_bits).to_bytes(2, "little")
             + bytes(sc12) + bytes(qs128))
+
+
+def prefill_x(T: int, K: int, seed: int) -> np.ndarray:
+    """float32 [T][K] prefill activations (see the module docstring)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x *= (10.0 ** rng.uniform(-1.0, 1.0, (T, 1))).astype(np.float32)
+    if K >= 64:
+        z = rng.integers(0, K // 32, T)
+        for t in range(T):
+            x[t, 32 * z[t]:32 * z[t] + 32] = 0.0
+    return np.ascontiguousarray(x)

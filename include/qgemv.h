@@ -180,6 +180,57 @@ size_t q4k_dsc_plane_bytes(int64_t N, int64_t K);
 qg_status q4k_build_dsc_plane(const uint8_t *w, float *dsc_out, int64_t N,
                               int64_t K, void *stream);
 
+/*
+ * q4_K prefill with 8-bit activations ("62 . r59 -- q4_K W_dsc plane +
+ * riders", section 2.1: the rank-1 rescale of each (chunk, row) integer dot
+ * product by (d*sc, -dmin*m) read from the W_dsc plane; section 3.2: the
+ * activations are quantized to 8 bits in a prepass before the integer matrix
+ * product).  For any number T of activation rows:
+ *     y[t,n] = sum_c d_a[t,c] * (dv[n,c] * sum_{k in c} q_w[n,k] * q_a[t,k]
+ *                               + mv[n,c] * sum_{k in c} q_a[t,k])
+ * The activation rule is not given on the page; this library uses, per block
+ * of 32 consecutive k of one row (one weight chunk): d_a = amax / 127 and
+ * q_a = x / d_a rounded half away from zero, both correctly rounded binary32
+ * operations; an all-zero block has d_a = 0 and q_a = 0.
+ */
+
+/* Workspace bytes qgemm_q4k_mmq needs for T activation rows of length K: the
+ * codes (T*K bytes, rounded up to 256) followed by T*(K/32) float2 (d_a,
+ * d_a * sum q_a).  0 when T < 1 or K is not a positive multiple of 256. */
+size_t q4k_mmq_workspace_bytes(int64_t T, int64_t K);
+
+/*
+ * q8_quantize_rows -- the activation prepass alone.
+ * x   : float32 [T][ldx], 4-byte aligned, ldx >= K; K a positive multiple of
+ *       32; T >= 0 (T == 0 enqueues nothing).
+ * qa  : int8 [T][K] codes out, 4-byte aligned.
+ * sda : float32 [T][K/32][2] out, 8-byte aligned: (d_a, d_a * sum of the
+ *       block's codes), the product rounded to binary32.
+ * qa, sda and x must not overlap.
+ */
+qg_status q8_quantize_rows(const float *x, int64_t ldx, int8_t *qa, float *sda,
+                           int64_t T, int64_t K, void *stream);
+
+/*
+ * qgemm_q4k_mmq -- the prefill product: prepass into `workspace`, then the
+ * int8 matrix-core product rescaled with the plane.  Two kernels on `stream`.
+ * x         : float32 [T][ldx], 4-byte aligned, ldx >= K.
+ * w         : raw q4_K [N][K/256][144] bytes, 16-byte aligned, < 4 GiB.
+ * dsc       : the W_dsc plane of w (q4k_build_dsc_plane), 16-byte aligned;
+ *             NULL is an error (QG_ERR_NULL_POINTER), never a silent fallback.
+ * y         : float32 [T][ldy] out, ldy >= N, 4-byte aligned.
+ * workspace : caller-owned device scratch of at least
+ *             q4k_mmq_workspace_bytes(T, K) bytes, 256-byte aligned; its
+ *             contents are overwritten; calls that share one workspace on
+ *             different streams race.
+ * T, N >= 0 (either 0 enqueues nothing), K a positive multiple of 256.
+ * y must not overlap x, w, dsc or the workspace, nor the workspace an input.
+ */
+qg_status qgemm_q4k_mmq(const float *x, int64_t ldx, const uint8_t *w,
+                        const float *dsc, float *y, int64_t ldy, int64_t T,
+                        int64_t N, int64_t K, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* Static English name of a status code ("QG_OK", ...). */
 const char *qg_status_string(qg_status s);
 

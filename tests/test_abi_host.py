@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     assert names == sorted(["qgemv_int4_blockwise", "qgemv_q4k", "qgemv_q4k_dsc", "gemv_bf16",
                             "q4k_dsc_plane_bytes", "q4k_build_dsc_plane", "qg_status_string",
                             "qg_last_error", "qg_last_launch", "qg_path_count", "qg_path_name",
-                            "qg_path_launches"])
+                            "qg_path_launches", "q4k_mmq_workspace_bytes", "q8_quantize_rows",
+                            "qgemm_q4k_mmq"])
 
 
 def test_library_exports_exactly_the_header():
@@ -134,6 +135,54 @@ def test_q4k_validation():
     assert _q4k(L, use_dsc=True, dsc=E) == QG_ERR_ALIAS
 
 
+def test_mmq_workspace_bytes():
+    # codes T*K (a multiple of 256 since K is), then T*(K/32) float2
+    assert q.q4k_mmq_workspace_bytes(1, 256) == 256 + 8 * 8
+    assert q.q4k_mmq_workspace_bytes(3, 512) == 1536 + 3 * 16 * 8
+    assert q.q4k_mmq_workspace_bytes(5, 256) == 1280 + 5 * 8 * 8
+    assert q.q4k_mmq_workspace_bytes(7, 256) == 1792 + 7 * 8 * 8
+    assert q.q4k_mmq_workspace_bytes(0, 256) == 0
+    assert q.q4k_mmq_workspace_bytes(4, 100) == 0
+    assert q.q4k_mmq_workspace_bytes(4, 128) == 0
+
+
+def _mmq(L, x=A, ldx=256, w=B, dsc=C, y=E, ldy=16, T=4, N=16, K=256, ws=D, wsb=None):
+    wsb = L.q4k_mmq_workspace_bytes(T, K) if wsb is None else wsb
+    return L.qgemm_q4k_mmq(x, ldx, w, dsc, y, ldy, T, N, K, ws, wsb, None)
+
+
+def test_mmq_validation():
+    L = q.load_library()
+    assert _mmq(L, x=None) == QG_ERR_NULL_POINTER
+    assert _mmq(L, dsc=None) == QG_ERR_NULL_POINTER
+    assert "no silent fallback" in L.qg_last_error().decode()
+    assert _mmq(L, ws=None) == QG_ERR_NULL_POINTER
+    assert _mmq(L, K=300, ldx=300) == QG_ERR_BAD_SHAPE
+    assert _mmq(L, K=128, ldx=128) == QG_ERR_BAD_SHAPE
+    assert _mmq(L, T=-1) == QG_ERR_BAD_SHAPE
+    assert _mmq(L, ldx=128) == QG_ERR_BAD_SHAPE
+    assert _mmq(L, ldy=8) == QG_ERR_BAD_SHAPE
+    assert _mmq(L, wsb=100) == QG_ERR_BAD_SHAPE
+    assert "workspace" in L.qg_last_error().decode()
+    assert _mmq(L, w=B + 8) == QG_ERR_MISALIGNED
+    assert _mmq(L, dsc=C + 8) == QG_ERR_MISALIGNED
+    assert _mmq(L, ws=D + 16) == QG_ERR_MISALIGNED
+    assert _mmq(L, x=A + 2) == QG_ERR_MISALIGNED
+    assert _mmq(L, y=B + 64) == QG_ERR_ALIAS          # y inside w
+    assert _mmq(L, ws=B) == QG_ERR_ALIAS              # workspace over w
+    assert _mmq(L, ws=E) == QG_ERR_ALIAS              # workspace over y
+    # empty problems enqueue nothing (no GPU needed)
+    assert _mmq(L, T=0) == QG_OK and _mmq(L, N=0) == QG_OK
+    assert L.qg_last_error().decode() == ""
+    # the prepass alone
+    assert L.q8_quantize_rows(None, 64, B, C, 2, 64, None) == QG_ERR_NULL_POINTER
+    assert L.q8_quantize_rows(A, 64, B, C, 2, 48, None) == QG_ERR_BAD_SHAPE
+    assert L.q8_quantize_rows(A, 32, B, C, 2, 64, None) == QG_ERR_BAD_SHAPE
+    assert L.q8_quantize_rows(A, 64, B, C + 4, 2, 64, None) == QG_ERR_MISALIGNED
+    assert L.q8_quantize_rows(A, 64, A + 16, C, 2, 64, None) == QG_ERR_ALIAS
+    assert L.q8_quantize_rows(A, 64, B, C, 0, 64, None) == QG_OK
+
+
 def test_plane_builder_validation():
     L = q.load_library()
     assert L.q4k_build_dsc_plane(None, C, 4, 256, None) == QG_ERR_NULL_POINTER
@@ -188,7 +237,7 @@ def test_product_package_does_not_import_the_oracle():
 def test_liveness_exports_on_the_host():
     # host-only functions: no GPU needed
     names = q.path_names()
-    assert len(names) == q.load_library().qg_path_count() == 14
+    assert len(names) == q.load_library().qg_path_count() == 16
     assert names[0] == "int4_dot2_persistent" and "q4k_persistent_plane" in names
     assert q.load_library().qg_path_name(-1) is None
     assert q.load_library().qg_path_name(len(names)) is None

@@ -19,12 +19,15 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqgemv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["qgemv_api.cpp", "int4_gemv.hip", "q4k_gemv.hip", "bf16_gemv.hip"]
+SOURCES = ["qgemv_api.cpp", "int4_gemv.hip", "q4k_gemv.hip", "bf16_gemv.hip", "q4k_mmq.hip"]
 
 # -packed-fp32-ops: never emit v_pk_{add,mul,fma}_f32 (kept off on this target).
+# Correctly rounded binary32 division: the 8-bit activation codes are decided
+# by a quotient.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
     "-Wno-unused-parameter", "-ffp-contract=fast", "-fvisibility=hidden",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]

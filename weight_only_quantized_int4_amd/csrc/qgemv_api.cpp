@@ -30,7 +30,7 @@ const char* const kPathNames[qg::kPathCount] = {
     "int4_dot2_persistent", "int4_dot2_tiled",      "int4_mfma_tiles", "int4_mfma_split",
     "int4_mfma_phased",     "q4k_persistent",       "q4k_persistent_plane", "q4k_tiled",
     "q4k_tiled_plane",      "q4k_plane_build",      "bf16_aligned",    "bf16_mfma_tiles",
-    "bf16_mfma_split",      "bf16_general"};
+    "bf16_mfma_split",      "bf16_general",         "q8_quantize",     "q4k_mmq"};
 
 void begin_call() {
   g_last_launch[0] = '\0';
@@ -269,6 +269,77 @@ qg_status q4k_build_dsc_plane(const uint8_t* w, float* dsc_out, int64_t N, int64
   return hip_status(qg::launch_q4k_build_plane(w, dsc_out, (int)N, (int)K,
                                                static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+size_t q4k_mmq_workspace_bytes(int64_t T, int64_t K) {
+  if (T < 1 || K < 256 || K % 256 != 0 || T > INT32_MAX || K > INT32_MAX) return 0;
+  return qg::q8_workspace_codes_bytes(T, K) + (size_t)T * (size_t)(K / 32) * 8;
+}
+
+qg_status q8_quantize_rows(const float* x, int64_t ldx, int8_t* qa, float* sda, int64_t T,
+                           int64_t K, void* stream) {
+  begin_call();
+  static const char fn[] = "q8_quantize_rows";
+  if (!x || !qa || !sda) return fail(QG_ERR_NULL_POINTER, "%s: x, qa and sda are required", fn);
+  if (T < 0 || K < 32 || K % 32 != 0)
+    return fail(QG_ERR_BAD_SHAPE, "%s: T = %lld, K = %lld (need T >= 0, K a positive multiple of 32)",
+                fn, (long long)T, (long long)K);
+  if (T > INT32_MAX || K > INT32_MAX) return fail(QG_ERR_BAD_SHAPE, "%s: T or K exceeds 2^31-1", fn);
+  if (qg_status s = check_ld(fn, "ldx", ldx, K)) return s;
+  if (!aligned(x, 4) || !aligned(qa, 4) || !aligned(sda, 8))
+    return fail(QG_ERR_MISALIGNED, "%s: x and qa must be 4-byte, sda 8-byte aligned", fn);
+  if (T == 0) return ok();
+  const Range rx = range_of(x, ((T - 1) * ldx + K) * 4), rq = range_of(qa, T * K),
+              rs = range_of(sda, T * (K / 32) * 8);
+  if (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs))
+    return fail(QG_ERR_ALIAS, "%s: qa, sda and x must not overlap", fn);
+  return hip_status(qg::launch_q8_quantize(x, ldx, qa, sda, (int)T, (int)K,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+qg_status qgemm_q4k_mmq(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
+                        int64_t ldy, int64_t T, int64_t N, int64_t K, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  begin_call();
+  static const char fn[] = "qgemm_q4k_mmq";
+  if (!x || !w || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w and y are required", fn);
+  if (!dsc) return fail(QG_ERR_NULL_POINTER, "%s: dsc plane is NULL (no silent fallback)", fn);
+  if (T < 0 || N < 0 || K < 256 || K % 256 != 0)
+    return fail(QG_ERR_BAD_SHAPE,
+                "%s: T = %lld, N = %lld, K = %lld (need T, N >= 0, K a positive multiple of 256)", fn,
+                (long long)T, (long long)N, (long long)K);
+  if (T > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+    return fail(QG_ERR_BAD_SHAPE, "%s: T, N or K exceeds 2^31-1", fn);
+  if (qg_status s = check_ld(fn, "ldx", ldx, K)) return s;
+  if (qg_status s = check_ld(fn, "ldy", ldy, N)) return s;
+  if (T == 0 || N == 0) return ok();
+  if (!workspace) return fail(QG_ERR_NULL_POINTER, "%s: workspace is required", fn);
+  const size_t need = q4k_mmq_workspace_bytes(T, K);
+  if (workspace_bytes < need)
+    return fail(QG_ERR_BAD_SHAPE, "%s: workspace of %zu bytes, need %zu (q4k_mmq_workspace_bytes)", fn,
+                workspace_bytes, need);
+  const int64_t wbytes = N * (K / 256) * 144;
+  if (wbytes >= kMaxTensorBytes)
+    return fail(QG_ERR_UNSUPPORTED, "%s: w is 4 GiB or larger (kernels use 32-bit offsets)", fn);
+  if (!aligned(w, 16) || !aligned(dsc, 16) || !aligned(workspace, 256) || !aligned(x, 4) ||
+      !aligned(y, 4))
+    return fail(QG_ERR_MISALIGNED,
+                "%s: w and dsc must be 16-byte, workspace 256-byte, x and y 4-byte aligned", fn);
+  const Range rx = range_of(x, ((T - 1) * ldx + K) * 4), rw = range_of(w, wbytes),
+              rd = range_of(dsc, N * K / 4), rws = range_of(workspace, (int64_t)need),
+              ry = range_of(y, ((T - 1) * ldy + N) * 4);
+  if (overlap(ry, rx) || overlap(ry, rw) || overlap(ry, rd) || overlap(ry, rws))
+    return fail(QG_ERR_ALIAS, "%s: y overlaps an input or the workspace", fn);
+  if (overlap(rws, rx) || overlap(rws, rw) || overlap(rws, rd))
+    return fail(QG_ERR_ALIAS, "%s: the workspace overlaps an input", fn);
+  int8_t* qa = static_cast<int8_t*>(workspace);
+  float* sda = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        qg::q8_workspace_codes_bytes(T, K));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = qg::launch_q8_quantize(x, ldx, qa, sda, (int)T, (int)K, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return hip_status(qg::launch_q4k_mmq(qa, sda, w, dsc, y, ldy, (int)T, (int)N, (int)K, st), fn);
 }
 
 }  // extern "C"

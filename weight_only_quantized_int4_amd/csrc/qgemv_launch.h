@@ -27,6 +27,8 @@ enum Path : int {
   kPathBf16MfmaTiles,
   kPathBf16MfmaSplit,
   kPathBf16General,
+  kPathQ8Quantize,
+  kPathQ4kMmq,
   kPathCount
 };
 
@@ -46,6 +48,14 @@ hipError_t launch_q4k_gemv(const float* x, int64_t ldx, const uint8_t* w,
 
 hipError_t launch_q4k_build_plane(const uint8_t* w, float* dsc, int N, int K,
                                   hipStream_t stream);
+
+// q4_K prefill (q4k_mmq.hip): the 8-bit activation prepass, the bytes its
+// codes take in a workspace (rounded up to 256), and the integer product.
+size_t q8_workspace_codes_bytes(int64_t T, int64_t K);
+hipError_t launch_q8_quantize(const float* x, int64_t ldx, int8_t* qa, float* sda, int T, int K,
+                              hipStream_t stream);
+hipError_t launch_q4k_mmq(const int8_t* qa, const float* sda, const uint8_t* w, const float* dsc,
+                          float* y, int64_t ldy, int T, int N, int K, hipStream_t stream);
 
 hipError_t launch_bf16_gemv(const uint16_t* x, int64_t ldx, const uint16_t* w,
                             int64_t ldw, void* y, int64_t ldy, int y_type, int M,

@@ -62,6 +62,9 @@ def load_library() -> ctypes.CDLL:
         "qg_path_count": (I32, []),
         "qg_path_name": (ctypes.c_char_p, [I32]),
         "qg_path_launches": (ctypes.c_uint64, [I32]),
+        "q4k_mmq_workspace_bytes": (ctypes.c_size_t, [I64, I64]),
+        "q8_quantize_rows": (St, [P, I64, P, P, I64, I64, P]),
+        "qgemm_q4k_mmq": (St, [P, I64, P, P, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -147,6 +150,30 @@ def q4k_build_dsc_plane(w: torch.Tensor, dsc_out: torch.Tensor, N: int, K: int,
     _check("q4k_build_dsc_plane", load_library().q4k_build_dsc_plane(
         _ptr(w), _ptr(dsc_out), N, K, _stream(stream)))
     return dsc_out
+
+
+def q4k_mmq_workspace_bytes(T: int, K: int) -> int:
+    return int(load_library().q4k_mmq_workspace_bytes(T, K))
+
+
+def q8_quantize_rows(x: torch.Tensor, qa: torch.Tensor, sda: torch.Tensor, stream=None):
+    """8-bit activation prepass.  x fp32 [T,K]; qa int8 [T,K]; sda fp32 [T,K/32,2]."""
+    T, K = x.shape
+    _check("q8_quantize_rows", load_library().q8_quantize_rows(
+        _ptr(x), _ld(x), _ptr(qa), _ptr(sda), T, K, _stream(stream)))
+    return qa, sda
+
+
+def qgemm_q4k_mmq(x: torch.Tensor, w: torch.Tensor, dsc: Optional[torch.Tensor], y: torch.Tensor,
+                  workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    """q4_K prefill: y[T,N] fp32 from x fp32 [T,K], raw q4_K w, its W_dsc plane
+    and a caller-owned workspace (uint8, >= q4k_mmq_workspace_bytes(T, K))."""
+    T, K = x.shape
+    N = w.shape[0]
+    _check("qgemm_q4k_mmq", load_library().qgemm_q4k_mmq(
+        _ptr(x), _ld(x), _ptr(w), _ptr(dsc), _ptr(y), _ld(y), T, N, K, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
 
 
 def last_launch() -> str:
