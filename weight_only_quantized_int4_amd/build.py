@@ -33,9 +33,15 @@ FLAGS = [
 ]
 
 
+# Per-source flags.  q4k_mmq.hip: keep matrix-core results in VGPRs (its
+# vector ALUs consume every result; the AGPR form adds a read per element).
+SOURCE_FLAGS = {"q4k_mmq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, "-x", "hip", *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, "-x", "hip", *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -132,20 +132,22 @@ __global__ __launch_bounds__(MmqShape<WT>::kThreads) void q4k_mmq_kernel(
   const uint32_t wrow = (uint32_t)nsb * kQ4kBlockBytes;
 
   // ---- global -> registers (one super-block), rows and tokens clamped ----
-  uint4 ra[S::kAPieces], rb[S::kBPieces], rs[S::kSPieces];
+  // (native vector types: arrays of the HIP uint4 struct were placed in
+  // scratch memory, which serialized every prefetch load)
+  u32x4 ra[S::kAPieces], rb[S::kBPieces], rs[S::kSPieces];
   float2 rp[S::kPEntries];
   auto fetch = [&](int sb) {
 #pragma unroll
     for (int i = 0; i < S::kAPieces; ++i) {
       const int p = tid + i * S::kThreads;
       const int tok = min(t0 + (p >> 4), T - 1);
-      ra[i] = *reinterpret_cast<const uint4*>(qa + (int64_t)tok * K + sb * 256 + (p & 15) * 16);
+      ra[i] = *reinterpret_cast<const u32x4*>(qa + (int64_t)tok * K + sb * 256 + (p & 15) * 16);
     }
 #pragma unroll
     for (int i = 0; i < S::kBPieces; ++i) {
       const int p = tid + i * S::kThreads;
       const int row = min(n0 + (p >> 3), N - 1);
-      rb[i] = *reinterpret_cast<const uint4*>(w + (row * wrow + sb * kQ4kBlockBytes + 16 + (p & 7) * 16));
+      rb[i] = *reinterpret_cast<const u32x4*>(w + (row * wrow + sb * kQ4kBlockBytes + 16 + (p & 7) * 16));
     }
 #pragma unroll
     for (int i = 0; i < S::kPEntries; ++i) {
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(MmqShape<WT>::kThreads) void q4k_mmq_kernel(
     for (int i = 0; i < S::kSPieces; ++i) {
       const int p = min(tid + i * S::kThreads, S::kBT * 4 - 1);  // p = token * 4 + pair
       const int tok = min(t0 + (p >> 2), T - 1);
-      rs[i] = *reinterpret_cast<const uint4*>(sda + (int64_t)tok * nchunk + sb * 8 + (p & 3) * 2);
+      rs[i] = *reinterpret_cast<const u32x4*>(sda + (int64_t)tok * nchunk + sb * 8 + (p & 3) * 2);
     }
   };
   // ---- registers -> LDS ----
@@ -165,12 +167,12 @@ __global__ __launch_bounds__(MmqShape<WT>::kThreads) void q4k_mmq_kernel(
 #pragma unroll
     for (int i = 0; i < S::kAPieces; ++i) {
       const int p = tid + i * S::kThreads;
-      *reinterpret_cast<uint4*>(As + (p >> 4) * kAStride + (p & 15) * 16) = ra[i];
+      *reinterpret_cast<u32x4*>(As + (p >> 4) * kAStride + (p & 15) * 16) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < S::kBPieces; ++i) {
       const int p = tid + i * S::kThreads;
-      *reinterpret_cast<uint4*>(Bs + (p >> 3) * kBStride + (p & 7) * 16) = rb[i];
+      *reinterpret_cast<u32x4*>(Bs + (p >> 3) * kBStride + (p & 7) * 16) = rb[i];
     }
 #pragma unroll
     for (int i = 0; i < S::kPEntries; ++i) Ps[tid + i * S::kThreads] = rp[i];
@@ -179,8 +181,8 @@ __global__ __launch_bounds__(MmqShape<WT>::kThreads) void q4k_mmq_kernel(
       const int p = tid + i * S::kThreads;
       if (p < S::kBT * 4) {
         const int tok = p >> 2, c = (p & 3) * 2;
-        Ss[c * S::kBT + tok] = make_float2(__uint_as_float(rs[i].x), __uint_as_float(rs[i].y));
-        Ss[(c + 1) * S::kBT + tok] = make_float2(__uint_as_float(rs[i].z), __uint_as_float(rs[i].w));
+        Ss[c * S::kBT + tok] = make_float2(__uint_as_float(rs[i][0]), __uint_as_float(rs[i][1]));
+        Ss[(c + 1) * S::kBT + tok] = make_float2(__uint_as_float(rs[i][2]), __uint_as_float(rs[i][3]));
       }
     }
   };
