@@ -174,6 +174,77 @@ def test_one_hot_probe_is_bit_exact():
         assert np.array_equal(got.view(np.uint32), wdq[:, ks].T.copy().view(np.uint32)), use_plane
 
 
+@pytest.mark.parametrize("K", [2048, 4096])
+def test_one_hot_probe_multi_row_is_bit_exact(K):
+    """M = 8: row r of x is one-hot at k_r; y must equal the oracle's
+    dequantized weight bitwise, through the header and the plane."""
+    N = 40
+    p = q4k_case(N, K, 78)
+    wdq = oracle.q4k_dequant(p.w, N, K).astype(np.float32)
+    wd = to_dev(p.w)
+    dsc = _plane(wd, N, K)
+    ks = list(range(0, K, 7)) + [K - 1]
+    say(f"q4k multi-row one-hot probe K={K}: {len(ks)} columns")
+    for use_plane in (False, True):
+        for i0 in range(0, len(ks), 8):
+            kk = ks[i0:i0 + 8]
+            M = len(kk)
+            x = torch.zeros((M, K), device=DEV)
+            for r, k in enumerate(kk):
+                x[r, k] = 1.0
+            y = torch.empty((M, N), device=DEV)
+            if use_plane:
+                q.qgemv_q4k_dsc(x, wd, dsc, y)
+            else:
+                q.qgemv_q4k(x, wd, y)
+            got = y.cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), wdq[:, kk].T.copy().view(np.uint32)), (use_plane, kk)
+
+
+@pytest.mark.parametrize("N,K,M", [(4096, 4096, 2), (4096, 4096, 8), (11008, 4096, 5),
+                                   (4096, 11008, 3), (4096, 11008, 8), (1000, 2048, 4)])
+def test_multi_row_layer_shapes_sampled(N, K, M):
+    p = q4k_case(N, K, 990 + M)
+    say(f"q4k multi-row N={N} K={K} M={M}")
+    xd, wd = to_dev(p.x[:M]), to_dev(p.w)
+    dsc = _plane(wd, N, K)
+    cols = sorted(set(np.random.default_rng(8).integers(0, N, 300).tolist()) | {0, 15, 16, N - 1})
+    yr, S = oracle.q4k_gemv(p.x, p.w, M, N, K, cols=cols)
+    outs = []
+    for use_plane in (False, True):
+        y = torch.full((M, N), float("nan"), device=DEV)
+        if use_plane:
+            q.qgemv_q4k_dsc(xd, wd, dsc, y)
+        else:
+            q.qgemv_q4k(xd, wd, y)
+        outs.append(y_host(y))
+        assert_accept(outs[-1][:, cols], yr, S, "f32", f"q4k {N}x{K} M={M} plane={use_plane}")
+    # one kernel template, one summation order: header and plane agree bitwise
+    assert np.array_equal(outs[0].view(np.uint64), outs[1].view(np.uint64))
+
+
+def test_row_magnitudes_and_unaligned_x():
+    """Rows of x at magnitudes from 1e-6 to 1e6 (and one 6e7 outlier), x at a
+    4-byte offset with a padded stride."""
+    N, K, M = 700, 4096, 6
+    p = q4k_case(N, K, 991)
+    x = p.x[:M].astype(np.float64)
+    x *= np.array([1e-6, 1e-2, 1.0, 3e2, 1e4, 1e6])[:, None]
+    x = x.astype(np.float32)
+    x[5, 100] = 6.0e7  # one large outlier in the last row
+    ldx = K + 3
+    buf = torch.zeros(1 + M * ldx, device=DEV)
+    for r in range(M):
+        buf[1 + r * ldx:1 + r * ldx + K] = torch.from_numpy(x[r]).to(DEV)
+    xd = buf[1:].as_strided((M, K), (ldx, 1))
+    wd = to_dev(p.w)
+    say(f"q4k scaled rows N={N} K={K} M={M}")
+    y = torch.full((M, N), float("nan"), device=DEV)
+    q.qgemv_q4k(xd, wd, y)
+    yr, S = oracle.q4k_gemv(x, p.w, M, N, K)
+    assert_accept(y_host(y), yr, S, "f32", "q4k scaled rows")
+
+
 def test_invariants():
     N, K, M = 512, 1024, 8
     p = q4k_case(N, K, 99)
