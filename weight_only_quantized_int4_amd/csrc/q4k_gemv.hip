@@ -285,7 +285,7 @@ void q4k_gemv_persistent(
   const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
 
   auto load = [&](Q4kPiece& st, int row, int it) {
-    row = row < N ? row : N - 1;  // ring refills past this wavefront's last row
+    row = row < N ? row : N - 1;  // a bound only: loaded items never pass the last row
     int p = j + kWave * it;
     p = p < P ? p : P - 1;  // idle lanes of a ragged last stride re-read a valid piece
     const uint32_t sb = (uint32_t)(p >> 2);
@@ -306,23 +306,24 @@ void q4k_gemv_persistent(
   };
 
   // D items in flight per lane: a register ring, each slot refilled as soon
-  // as it is consumed (unconditionally; past the last item the row index is
-  // clamped, so surplus loads re-read cached bytes).
+  // as it is consumed, as long as items remain (the branch is uniform across
+  // the wavefront).
   Q4kPiece ring[D];
   int lrow = first, lit = 0;  // next item to load
-  // (unconditional: a wavefront without rows loads clamped ones and never
-  // consumes them)
   auto fill_ring = [&] {
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-      load(ring[k], lrow, lit);
+      if (k < nitems) load(ring[k], lrow, lit);
       advance(lrow, lit);
     }
   };
 
   // Stage x; the chunk sums come out of the same pass when x is 16-byte
-  // aligned (8 consecutive lanes hold one 32-element chunk).  The ring's
-  // first loads go out right behind the first x loads.
+  // aligned (8 consecutive lanes hold one 32-element chunk).  Decoding in
+  // the kernel, a thread issues its weight loads once its x slots are in:
+  // behind the weight stream of the whole grid, x would arrive late (measured
+  // 0.2-0.5 us per call on the 7B layer shapes).  With the plane, the ring's
+  // first loads go out right behind the x loads (measured better there).
   if (x_vec16) {
     // K is a multiple of 256, so M * K / 4 is a multiple of 64: whole
     // wavefronts stage together and the 8-lane DPP sum is well defined.
@@ -341,7 +342,13 @@ void q4k_gemv_persistent(
           const float part = group_sum<8>((v.x + v.y) + (v.z + v.w));
           if ((i & 7) == 0) sx[m * K32 + (i >> 3)] = part;
         },
-        fill_ring);
+        [&] {
+          if constexpr (DSC) fill_ring();
+        });
+    if constexpr (!DSC) {
+      __builtin_amdgcn_sched_barrier(0);
+      fill_ring();
+    }
     __syncthreads();
   } else {
     fill_ring();
@@ -441,7 +448,7 @@ void q4k_gemv_persistent(
     for (int k = 0; k < D; ++k) {
       consume(ring[k], prow, pit);
       advance(prow, pit);
-      load(ring[k], lrow, lit);
+      if (u + k + D < nitems) load(ring[k], lrow, lit);
       advance(lrow, lit);
     }
   }
