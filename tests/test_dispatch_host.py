@@ -41,7 +41,17 @@ def fake_abi(monkeypatch):
     monkeypatch.setattr(qgemv, "q4k_dsc_plane_bytes", lambda N, K: N * K // 4)
     monkeypatch.setattr(qgemv, "qgemv_int4_blockwise", int4)
     monkeypatch.setattr(qgemv, "gemv_bf16", bf16)
+
+    def mmq(x, w, dsc, y, workspace, stream=None):
+        assert dsc is not None and workspace.numel() >= x.shape[0] * 10
+        calls.append(("mmq", x.shape[0], workspace.numel()))
+        return y
+
+    monkeypatch.setattr(qgemv, "qgemm_q4k_mmq", mmq)
+    monkeypatch.setattr(qgemv, "q4k_mmq_workspace_bytes", lambda T, K: T * 10)
+    monkeypatch.setattr(qgemv, "_stream", lambda stream: 0 if stream is None else int(stream))
     monkeypatch.delenv("QGEMV_Q4K_DSC", raising=False)
+    monkeypatch.delenv("QGEMV_Q4K_MMQ_MIN_ROWS", raising=False)
     dispatch.reset_liveness()
     yield calls
     dispatch.reset_liveness()
@@ -116,3 +126,44 @@ def test_int4_and_bf16_row_groups(fake_abi, M, groups):
     yb = dispatch.bf16_linear(xb, torch.zeros((32, 64), dtype=torch.bfloat16))
     assert yb.shape == (M, 32) and yb.dtype == torch.bfloat16
     assert [c[1] for c in fake_abi if c[0] == "bf16"] == groups
+
+
+def test_prefill_arm_is_opt_in(fake_abi, monkeypatch):
+    w = _q4k_weights()
+    x = torch.zeros((40, 512))
+    # without a plane the arm is never taken
+    _, label = dispatch.q4k_linear(x, w, prefill_min_rows=32)
+    assert label == dispatch.LABEL_OFF and fake_abi[-1] == ("q4k", 8)
+    assert dispatch.register_q4k_plane(w)
+    _, label = dispatch.q4k_linear(x, w)  # default: off
+    assert label == dispatch.LABEL_PLANE and fake_abi[-1] == ("q4k_dsc", 8)
+    monkeypatch.setenv("QGEMV_Q4K_MMQ_MIN_ROWS", "32")
+    _, label = dispatch.q4k_linear(x, w)
+    assert label == dispatch.LABEL_MMQ and fake_abi[-1] == ("mmq", 40, 400)
+    _, label = dispatch.q4k_linear(x[:31], w)  # below the threshold: row groups
+    assert label == dispatch.LABEL_PLANE
+    _, label = dispatch.q4k_linear(x, w, prefill_min_rows=0)  # the argument wins
+    assert label == dispatch.LABEL_PLANE
+    _, label = dispatch.q4k_linear(x, w, use_plane=False)  # no plane, no arm
+    assert label == dispatch.LABEL_OFF
+    assert dispatch.liveness()[dispatch.LABEL_MMQ] == 1
+    monkeypatch.setenv("QGEMV_Q4K_MMQ_MIN_ROWS", "many")
+    with pytest.raises(ValueError):
+        dispatch.q4k_linear(x, w)
+    dispatch.unregister_q4k_plane(w)
+
+
+def test_prefill_workspace_grows_per_stream(fake_abi):
+    w = _q4k_weights()
+    assert dispatch.register_q4k_plane(w)
+    dispatch.q4k_linear(torch.zeros((40, 512)), w, prefill_min_rows=16)
+    ws40 = dispatch._workspaces[(None, 0)]
+    dispatch.q4k_linear(torch.zeros((20, 512)), w, prefill_min_rows=16)
+    assert dispatch._workspaces[(None, 0)] is ws40  # large enough: reused
+    dispatch.q4k_linear(torch.zeros((64, 512)), w, prefill_min_rows=16)
+    assert dispatch._workspaces[(None, 0)].numel() == 640  # grown
+    dispatch.q4k_linear(torch.zeros((16, 512)), w, prefill_min_rows=16, stream=7)
+    assert dispatch._workspaces[(None, 7)].numel() == 160  # its own stream, its own buffer
+    assert [c[2] for c in fake_abi if c[0] == "mmq"] == [400, 400, 640, 160]
+    dispatch._workspaces.clear()
+    dispatch.unregister_q4k_plane(w)

@@ -1,14 +1,17 @@
 """GPU behaviour of the dispatch layer and the liveness record (MI355X):
 the registered q4_K plane is used and agrees bitwise with in-kernel decode, a
 failed registration falls back with its label, qg_last_launch names the
-kernels of the last call, the per-path counters move, and row groups beyond
-8 rows of x match the oracle."""
+kernels of the last call, the per-path counters move, row groups beyond 8
+rows of x match the oracle, and the opt-in prefill arm gives the prefill
+product's result."""
 import warnings
 
 import numpy as np
 import pytest
 import torch
 
+import datagen
+import oracle
 import weight_only_quantized_int4_amd as q
 from weight_only_quantized_int4_amd import dispatch
 from gpu_cases import (DEV, assert_accept, bf16_case, bf16_dev, f16_dev, int4_case, int4_ref,
@@ -44,7 +47,7 @@ def test_q4k_plane_registry_and_liveness():
     yr, S = q4k_ref(N, K, 430)
     assert_accept(y_host(y_plane), yr[:3], S[:3], "f32", "dispatch q4k plane")
     assert dispatch.liveness() == {dispatch.LABEL_PLANE: 1, dispatch.LABEL_OFF: 2,
-                                   dispatch.LABEL_FALLBACK: 0}
+                                   dispatch.LABEL_FALLBACK: 0, dispatch.LABEL_MMQ: 0}
     dispatch.unregister_q4k_plane(wd)
 
 
@@ -121,6 +124,35 @@ def test_row_groups_match_the_oracle(M):
     xb = np.concatenate([b.x, b.x ^ np.uint16(0x8000)])[:M]
     yb = dispatch.bf16_linear(bf16_dev(xb), bf16_dev(b.w),
                               torch.empty((M, 1536), dtype=torch.float32, device=DEV))
-    import oracle
     ybr, Sb = oracle.bf16_gemv(np.ascontiguousarray(xb), b.w, M, 1536, 1536, 1536, 1536)
     assert_accept(y_host(yb), ybr, Sb, "f32", f"bf16 row groups M={M}")
+
+
+def test_prefill_arm_is_the_prefill_product():
+    N, K, T = 300, 1024, 40
+    p = q4k_case(N, K, 435)
+    wd = to_dev(p.w)
+    x = to_dev(datagen.prefill_x(T, K, 436))
+    say(f"dispatch q4k prefill arm T={T} N={N} K={K}")
+    dispatch.reset_liveness()
+    assert dispatch.register_q4k_plane(wd)
+    y_rows, label = dispatch.q4k_linear(x, wd)  # default: no prefill arm
+    assert label == dispatch.LABEL_PLANE
+    y_mmq, label = dispatch.q4k_linear(x, wd, prefill_min_rows=32)
+    assert label == dispatch.LABEL_MMQ
+    launches = q.last_launch()
+    assert "q8_quantize" in launches and "q4k_mmq" in launches
+    ws = torch.empty(q.q4k_mmq_workspace_bytes(T, K), dtype=torch.uint8, device=DEV)
+    y_direct = q.qgemm_q4k_mmq(x, wd, dispatch.q4k_plane_of(wd), torch.empty((T, N), device=DEV), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_mmq, y_direct)
+    _, label = dispatch.q4k_linear(x[:20], wd, prefill_min_rows=32)  # fewer rows: row groups
+    assert label == dispatch.LABEL_PLANE
+    assert dispatch.liveness()[dispatch.LABEL_MMQ] == 1
+    yr, S = oracle.q4k_mmq(datagen.prefill_x(T, K, 436), p.w, T, N, K)
+    ok, worst = oracle.accept(y_host(y_mmq), yr, S, "f32", rtol=oracle.RTOL_MMQ)
+    assert ok, worst
+    # the default (row groups) is the GEMV, within the GEMV tolerance
+    yg, Sg = oracle.q4k_gemv(datagen.prefill_x(T, K, 436), p.w, T, N, K)
+    assert_accept(y_host(y_rows), yg, Sg, "f32", "dispatch q4k rows T=40")
+    dispatch.unregister_q4k_plane(wd)

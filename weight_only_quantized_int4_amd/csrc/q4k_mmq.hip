@@ -21,9 +21,10 @@
 // The 4-bit quants need no reordering: chunk 2g (2g+1) of a super-block is the
 // low (high) nibble of quant bytes 32g..32g+31, so lane group j takes bytes
 // 32g+8j..+8 for both chunks, and the A operand takes the activations of the
-// same k.  A wavefront owns 32 activation rows x 64 weight rows (2 x 4 MFMA
-// blocks); the workgroup stages one super-block (256 k) of its codes, quant
-// bytes, plane entries and activation scales in LDS and prefetches the next
+// same k.  A wavefront owns 16 activation rows x 64 weight rows (1 x 4 MFMA
+// blocks); a workgroup of 4 x 2 wavefronts covers 64 activation rows x 128
+// weight rows, stages one super-block (256 k) of its codes, quant bytes,
+// plane entries and activation scales in LDS and prefetches the next
 // super-block into registers meanwhile.  The rescale runs in fp32 per chunk.
 #include "qgemv_device.h"
 #include "qgemv_launch.h"
@@ -83,15 +84,16 @@ __global__ __launch_bounds__(kPrepassThreads) void q8_quantize_kernel(
 // Product
 // ---------------------------------------------------------------------------
 
-constexpr int kWaveTokens = 32;    // activation rows per wavefront (2 MFMA blocks)
 constexpr int kWaveRows = 64;      // weight rows per wavefront (4 MFMA blocks)
 constexpr int kRowWaves = 2;       // wavefronts along the weight rows
 constexpr int kBN = kWaveRows * kRowWaves;  // weight rows per workgroup
 constexpr int kAStride = 256 + 16;  // LDS bytes per staged activation row (one super-block)
 constexpr int kBStride = 128 + 16;  // LDS bytes per staged weight row (its 128 quant bytes)
 
-template <int WT>
+// WT wavefronts along the activation rows, each with TB blocks of 16 rows.
+template <int WT, int TB>
 struct MmqShape {
+  static constexpr int kWaveTokens = 16 * TB;  // activation rows per wavefront
   static constexpr int kThreads = WT * kRowWaves * kWave;
   static constexpr int kBT = WT * kWaveTokens;  // activation rows per workgroup
   static constexpr int kABytes = kBT * kAStride;
@@ -109,11 +111,11 @@ struct MmqShape {
                 "staging pieces must divide evenly");
 };
 
-template <int WT>
-__global__ __launch_bounds__(MmqShape<WT>::kThreads) void q4k_mmq_kernel(
+template <int WT, int TB>
+__global__ __launch_bounds__((MmqShape<WT, TB>::kThreads)) void q4k_mmq_kernel(
     const int8_t* __restrict__ qa, const float2* __restrict__ sda, const uint8_t* __restrict__ w,
     const float2* __restrict__ dsc, float* __restrict__ y, int64_t ldy, int T, int N, int K) {
-  using S = MmqShape<WT>;
+  using S = MmqShape<WT, TB>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   char* As = lds;
   char* Bs = As + S::kABytes;
@@ -187,17 +189,17 @@ __global__ __launch_bounds__(MmqShape<WT>::kThreads) void q4k_mmq_kernel(
     }
   };
 
-  f32x4 acc[2][4];
+  f32x4 acc[TB][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TB; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const i32x4 zero = {0, 0, 0, 0};
 
   // LDS byte offsets of this lane's operands
-  const int a_off0 = (wt * kWaveTokens + n16) * kAStride + 8 * g;    // + 16 * tb rows, + 32 * cc
+  const int a_off0 = (wt * S::kWaveTokens + n16) * kAStride + 8 * g;  // + 16 * tb rows, + 32 * cc
   const int b_off0 = (wn * kWaveRows + n16) * kBStride + 8 * g;      // + 16 * rb rows, + 32 * pair
-  const int s_tok0 = wt * kWaveTokens + 4 * g;                        // + 16 * tb, tokens +0..3
+  const int s_tok0 = wt * S::kWaveTokens + 4 * g;                     // + 16 * tb, tokens +0..3
   const int p_row0 = wn * kWaveRows + n16;                            // + 16 * rb
 
   fetch(0);
@@ -215,17 +217,17 @@ __global__ __launch_bounds__(MmqShape<WT>::kThreads) void q4k_mmq_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int cc = pair * 2 + h;
-        int64_t av[2];
+        int64_t av[TB];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < TB; ++tb)
           av[tb] = *reinterpret_cast<const int64_t*>(As + a_off0 + tb * 16 * kAStride + cc * 32);
         int64_t bv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           bv[r] = (int64_t)((h ? (braw[r] >> 4) : braw[r]) & 0x0F0F0F0F0F0F0F0Full);
-        i32x4 dd[2][4];
+        i32x4 dd[TB][4];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             dd[tb][r] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[tb], bv[r], zero, 0, 0, 0);
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(MmqShape<WT>::kThreads) void q4k_mmq_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) pc[r] = Ps[cc * kBN + p_row0 + r * 16];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
+        for (int tb = 0; tb < TB; ++tb) {
           const float4* sp = reinterpret_cast<const float4*>(Ss + cc * S::kBT + s_tok0 + tb * 16);
           const float4 s01 = sp[0], s23 = sp[1];
           const float da[4] = {s01.x, s01.z, s23.x, s23.z};
@@ -262,24 +264,24 @@ __global__ __launch_bounds__(MmqShape<WT>::kThreads) void q4k_mmq_kernel(
 
   // ---- epilogue: lane holds activation rows 4g..4g+3 of weight row n16 ----
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+  for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = n0 + wn * kWaveRows + r * 16 + n16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + wt * kWaveTokens + tb * 16 + 4 * g + i;
+        const int tok = t0 + wt * S::kWaveTokens + tb * 16 + 4 * g + i;
         if (tok < T && row < N) y[(int64_t)tok * ldy + row] = acc[tb][r][i];
       }
     }
 }
 
-template <int WT>
+template <int WT, int TB>
 hipError_t launch_mmq_wt(const int8_t* qa, const float2* sda, const uint8_t* w, const float2* dsc,
                          float* y, int64_t ldy, int T, int N, int K, hipStream_t stream) {
-  using S = MmqShape<WT>;
+  using S = MmqShape<WT, TB>;
   const dim3 grid((N + kBN - 1) / kBN, (T + S::kBT - 1) / S::kBT);
-  auto kern = q4k_mmq_kernel<WT>;
+  auto kern = q4k_mmq_kernel<WT, TB>;
   const hipError_t e = allow_lds(kern, S::kLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(S::kThreads), S::kLds, stream, qa, sda, w, dsc, y, ldy, T, N,
@@ -309,11 +311,12 @@ hipError_t launch_q4k_mmq(const int8_t* qa, const float* sda, const uint8_t* w, 
                           float* y, int64_t ldy, int T, int N, int K, hipStream_t stream) {
   const float2* s2 = reinterpret_cast<const float2*>(sda);
   const float2* p2 = reinterpret_cast<const float2*>(dsc);
-  // 128 activation rows per workgroup when that still gives every CU a
-  // workgroup, else 64.
-  const int64_t tiles128 = (int64_t)((N + kBN - 1) / kBN) * ((T + 127) / 128);
-  if (tiles128 >= 256) return launch_mmq_wt<4>(qa, s2, w, p2, y, ldy, T, N, K, stream);
-  return launch_mmq_wt<2>(qa, s2, w, p2, y, ldy, T, N, K, stream);
+  // One block of 16 activation rows per wavefront (TB = 1) and 4 wavefronts
+  // along the activation rows measured fastest for T = 8 .. 2048 on the 7B
+  // layer shapes (against 2 blocks per wavefront and 2 wavefronts: twice the
+  // wavefronts for the same work, 111 instead of 157-184 VGPRs, and the stalls
+  // of one wavefront overlap another's; 4096 x 4096 at T = 512: 81 -> 61 us).
+  return launch_mmq_wt<4, 1>(qa, s2, w, p2, y, ldy, T, N, K, stream);
 }
 
 }  // namespace qg

@@ -14,10 +14,20 @@ must carry a visible label", because parity cannot see the path.  Labels
                           path is switched off (QGEMV_Q4K_DSC=0, or
                           use_plane=False) -- the page's contrast switch
     in-kernel(fallback!)  a registration was attempted and failed
+    mmq(q8 activations)   the prefill product (8-bit activations, the plane)
 
 Rows (the AstrAI backend commit list: decode-time linear layers go to the GEMV
 for small M): the kernels take M = 1..8; these wrappers take any M >= 1 and
 run row groups of at most 8 rows of x (each group reads the weights again).
+
+Prefill arm (the same page, section 3.2: the dispatch arm that quantizes the
+activations): with a plane registered, a q4_K call with at least
+``prefill_min_rows`` rows of x (argument, else QGEMV_Q4K_MMQ_MIN_ROWS; 0 =
+never, the default) goes to the prefill product instead of row groups.  It is
+opt-in because its result is a different computation (activations rounded to 8
+bits per block of 32).  Measured on the 7B layer shapes with cold weights, the
+product overtakes the row groups from about 16-32 rows of x.  Its workspace is
+kept per (device, stream) and grows on demand.
 
 Everything here is argument handling; every output element is computed by the
 library's HIP kernels.  ``explain()`` returns the library's description of the
@@ -38,16 +48,43 @@ MAX_ROWS = 8
 LABEL_PLANE = "dsc-plane"
 LABEL_OFF = "in-kernel(dsc=off)"
 LABEL_FALLBACK = "in-kernel(fallback!)"
+LABEL_MMQ = "mmq(q8 activations)"
 
 _lock = threading.Lock()
 _planes = {}   # weight device pointer -> plane tensor
 _failed = {}   # weight device pointer -> reason the registration failed
 _warned = False
-_liveness = {LABEL_PLANE: 0, LABEL_OFF: 0, LABEL_FALLBACK: 0}
+_liveness = {LABEL_PLANE: 0, LABEL_OFF: 0, LABEL_FALLBACK: 0, LABEL_MMQ: 0}
+_workspaces = {}  # (device index, stream handle) -> uint8 workspace of the prefill product
 
 
 def _plane_enabled() -> bool:
     return os.environ.get("QGEMV_Q4K_DSC", "1") != "0"
+
+
+def _mmq_min_rows() -> int:
+    v = os.environ.get("QGEMV_Q4K_MMQ_MIN_ROWS", "0")
+    try:
+        return max(0, int(v))
+    except ValueError:
+        raise ValueError(f"QGEMV_Q4K_MMQ_MIN_ROWS must be an integer, got {v!r}") from None
+
+
+def _workspace(device: torch.device, stream, nbytes: int) -> torch.Tensor:
+    """The prefill workspace of (device, stream), at least ``nbytes`` long.
+    Growing it first waits for the work queued on that stream, which may
+    still read the old buffer."""
+    handle = _q._stream(stream)
+    key = (device.index, handle)
+    with _lock:
+        ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        if ws is not None and device.type == "cuda":
+            torch.cuda.ExternalStream(handle, device=device).synchronize()
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        with _lock:
+            _workspaces[key] = ws
+    return ws
 
 
 def q4k_shape(w: torch.Tensor) -> Tuple[int, int]:
@@ -103,9 +140,12 @@ def _count(label: str) -> None:
 
 
 def q4k_linear(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = None,
-               use_plane: bool = True, stream=None) -> Tuple[torch.Tensor, str]:
+               use_plane: bool = True, stream=None,
+               prefill_min_rows: Optional[int] = None) -> Tuple[torch.Tensor, str]:
     """y[M, N] = x[M, K] . dequant(w)^T for raw q4_K weights, through the
-    registered plane when there is one.  Returns (y, liveness label)."""
+    registered plane when there is one; with a plane and at least
+    ``prefill_min_rows`` rows of x (> 0), through the prefill product.
+    Returns (y, liveness label)."""
     global _warned
     N, K = q4k_shape(w)
     M = x.shape[0]
@@ -128,6 +168,12 @@ def q4k_linear(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = Non
                           stacklevel=2)
     else:
         label = LABEL_OFF
+    min_rows = _mmq_min_rows() if prefill_min_rows is None else prefill_min_rows
+    if dsc is not None and min_rows > 0 and M >= min_rows:
+        ws = _workspace(x.device, stream, _q.q4k_mmq_workspace_bytes(M, K))
+        _q.qgemm_q4k_mmq(x, w, dsc, y, ws, stream)
+        _count(LABEL_MMQ)
+        return y, LABEL_MMQ
     for m0, m1 in _row_groups(M):
         if dsc is not None:
             _q.qgemv_q4k_dsc(x[m0:m1], w, dsc, y[m0:m1], stream)
