@@ -113,12 +113,23 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
       if (j == 0 && rows[i] < N) store_out(y, m * ldy + rows[i], tot[i * M + m], y_type);
 }
 
+constexpr int kGenStage = 8;
+constexpr int kGenShortRow = 128;  // elements
+
+// LDS layout of the general kernel's staged x: a pad float after every 8.
+__host__ __device__ constexpr int gen_x_index(int e) { return e + (e >> 3); }
+__host__ __device__ constexpr int gen_x_stride(int KC) { return gen_x_index(KC + 8) + 1; }
+
 template <int M, int LPR>
 __global__ __launch_bounds__(kBlock) void bf16_gemv_general(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw,
     void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int KC) {
-  extern __shared__ float xf[];  // [M][KC + 8] fp32, chunk plus halo
-  const int XS = KC + 8;
+  // [M][gen_x_stride(KC)] fp32, chunk plus halo; element e of a row sits at
+  // e + e / 8 (one pad float after every 8), so the lanes of a row, whose
+  // pieces start 8 elements apart, read banks 9 floats apart (no conflicts;
+  // unpadded, every read of a wavefront hit 4 banks).
+  extern __shared__ float xf[];
+  const int XS = gen_x_stride(KC);
   constexpr int S = kBlock / LPR;
   const int tid = threadIdx.x;
   const int slot = tid / LPR;
@@ -137,14 +148,86 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_general(
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.f;
 
+  auto body_piece = [&](const uint4 v, int s0, int kc) {
+    const float wv[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                         bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float* xp = xf + m * XS;
+      float a = acc[m];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = __builtin_fmaf(wv[e], xp[gen_x_index(s0 - kc + e)], a);
+      acc[m] = a;
+    }
+  };
+  // The first chunk's first body piece of this lane is loaded behind the
+  // first round of x loads, so the two latencies overlap.
+  uint4 pre = {0u, 0u, 0u, 0u};
+  const int e_hi0 = min(KC, K) - h;
+  const bool have_pre = live && j < min(nbody, e_hi0 > 0 ? (e_hi0 + 7) >> 3 : 0);
+
 #pragma unroll 1
   for (int kc = 0; kc < K; kc += KC) {
     const int kn = min(KC, K - kc);
     const int ext = min(kn + 8, K - kc);
     __syncthreads();
-    for (int t = tid; t < M * ext; t += kBlock) {
-      const int m = t / ext, e = t - m * ext;
-      xf[m * XS + e] = __uint_as_float((uint32_t)x[m * ldx + kc + e] << 16);
+    // x rows are read as aligned 16-byte words (8 elements each; a word that
+    // holds an element of the row lies in the same page as that element, so
+    // its other bytes are readable), kGenStage words in flight per thread
+    // before the first wait.  Slot q of a thread is word tid + r * kBlock of
+    // row m, q = m * per + r (the same for the whole workgroup, counted
+    // without divisions).
+    const int per = ((ext + 14) / 8 + kBlock - 1) / kBlock;  // >= words of any row
+    // Short rows (a few words) are staged one element per thread: cheaper
+    // than kGenStage word slots per thread that mostly hold nothing.
+    const int nq = ext <= kGenShortRow ? 0 : M * per;
+    if (nq == 0) {
+      for (int t = tid; t < M * ext; t += kBlock) {
+        const int m = t / ext, e = t - m * ext;
+        xf[m * XS + gen_x_index(e)] = __uint_as_float((uint32_t)x[m * ldx + kc + e] << 16);
+      }
+      if (kc == 0 && have_pre) pre = load_stream16(wr + h + 8 * j);
+    }
+    int m0 = 0, r0 = 0;      // (m, r) of slot q0
+    for (int q0 = 0; q0 < nq; q0 += kGenStage) {
+      uint4 v[kGenStage];
+      int mu[kGenStage], wu[kGenStage];
+      {
+        int m = m0, r = r0;
+#pragma unroll
+        for (int u = 0; u < kGenStage; ++u) {
+          const int mc = min(m, M - 1);
+          const uintptr_t rb = reinterpret_cast<uintptr_t>(x + mc * ldx + kc);
+          const int skip = (int)((rb & 15u) >> 1);  // elements before the row in its first word
+          const int nw = (skip + ext + 7) >> 3;     // words holding the row
+          const int wi = tid + r * kBlock;
+          mu[u] = m < M && wi < nw ? m : -1;         // -1: nothing to store
+          wu[u] = 8 * wi - skip;                     // element of the word's first half-word
+          v[u] = *reinterpret_cast<const uint4*>((rb & ~(uintptr_t)15) +
+                                                 16 * (uintptr_t)min(wi, nw - 1));
+          if (++r == per) { r = 0; ++m; }
+        }
+        m0 = m;
+        r0 = r;
+      }
+      if (kc == 0 && q0 == 0 && have_pre) {
+        __builtin_amdgcn_sched_barrier(0);
+        pre = load_stream16(wr + h + 8 * j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int u = 0; u < kGenStage; ++u) {
+        if (mu[u] >= 0) {  // (whole wavefronts skip the words past short rows)
+          const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int e = wu[u] + k;
+            if (e >= 0 && e < ext)
+              xf[mu[u] * XS + gen_x_index(e)] =
+                  __uint_as_float(k & 1 ? wd[k >> 1] & 0xFFFF0000u : wd[k >> 1] << 16);
+          }
+        }
+      }
     }
     __syncthreads();
     if (!live) continue;
@@ -153,31 +236,25 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_general(
     for (int k = kc + j; k < min(h, kc + kn); k += LPR) {
       const float wf = __uint_as_float((uint32_t)wr[k] << 16);
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(wf, xf[m * XS + (k - kc)], acc[m]);
+      for (int m = 0; m < M; ++m)
+        acc[m] = __builtin_fmaf(wf, xf[m * XS + gen_x_index(k - kc)], acc[m]);
     }
     // body: 16-byte pieces starting at h + 8i that begin inside this chunk
     const int i_lo = (kc > h) ? (kc - h + 7) >> 3 : 0;
     const int e_hi = kc + kn - h;
     const int i_hi = min(nbody, e_hi > 0 ? (e_hi + 7) >> 3 : 0);
-    for (int i = i_lo + j; i < i_hi; i += LPR) {
-      const int s0 = h + 8 * i;
-      const uint4 v = load_stream16(wr + s0);
-      const float wv[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                           bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const float* xp = xf + m * XS + (s0 - kc);
-        float a = acc[m];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = __builtin_fmaf(wv[e], xp[e], a);
-        acc[m] = a;
-      }
+    int i = i_lo + j;
+    if (kc == 0 && have_pre) {  // i == j here
+      body_piece(pre, h + 8 * j, kc);
+      i += LPR;
     }
+    for (; i < i_hi; i += LPR) body_piece(load_stream16(wr + h + 8 * i), h + 8 * i, kc);
     // tail: k in [t0, K)
     for (int k = max(kc, t0) + j; k < kc + kn; k += LPR) {
       const float wf = __uint_as_float((uint32_t)wr[k] << 16);
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(wf, xf[m * XS + (k - kc)], acc[m]);
+      for (int m = 0; m < M; ++m)
+        acc[m] = __builtin_fmaf(wf, xf[m * XS + gen_x_index(k - kc)], acc[m]);
     }
   }
 
@@ -398,9 +475,10 @@ hipError_t launch_general(const uint16_t* x, int64_t ldx, const uint16_t* w, int
                           int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
   constexpr int S = kBlock / LPR;
   const int grid = (N + S - 1) / S;
-  int KC = (kLdsXBudget / (4 * M) - 8) & ~7;
+  // largest multiple of 8 whose padded rows fit the budget
+  int KC = ((kLdsXBudget / (4 * M) - 10) * 8 / 9) & ~7;
   if (KC > K) KC = K;
-  const size_t shmem = (size_t)M * (KC + 8) * 4;
+  const size_t shmem = (size_t)M * gen_x_stride(KC) * 4;
   hipLaunchKernelGGL((bf16_gemv_general<M, LPR>), dim3(grid), dim3(kBlock), shmem, stream, x, ldx,
                      w, ldw, y, ldy, y_type, N, K, KC);
   note_launch(kPathBf16General, M, grid, kBlock, shmem);
