@@ -77,7 +77,8 @@ def test_output_types(out_dtype):
 
 
 def test_long_unaligned_k_multi_chunk():
-    # M = 8 stages 2008 elements per pass in the general path: K = 6911 -> 4 passes
+    # M = 8 stages 1776 elements per pass in the general path: K = 6911 -> 4 passes;
+    # x rows start at odd element offsets (ldx = 6911), each row its own alignment
     N, K, M = 200, 6911, 8
     p = bf16_case(N, K, 340)
     say("bf16 general path multi-chunk")
