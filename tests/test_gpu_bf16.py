@@ -3,7 +3,7 @@
 Workloads: (1536 x 1536), (256 x 1536), (1536 x 6912), (6912 x 1536) at
 M = 1..8; the unaligned-tail path with K in {7, 12, 100, 1534} at N in
 {256, 1536}; 2-byte base offsets on x and W; every output type; the current
-stream; invariants.
+stream; invariants; seeded random shapes, offsets and row strides.
 """
 import numpy as np
 import pytest
@@ -157,3 +157,28 @@ def test_invariants_and_stream():
     assert torch.cuda.default_stream().query()
     s.synchronize()
     assert np.array_equal(y_host(y2), base)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_shapes_offsets_and_strides(case):
+    """Seeded random N, K, M, 2-byte base offsets and row strides (padded,
+    odd): mostly the unaligned path, where x rows are staged from aligned
+    16-byte words and every row of x and W has its own alignment."""
+    rng = np.random.default_rng(5000 + case)
+    N, K, M = int(rng.integers(1, 700)), int(rng.integers(1, 3000)), int(rng.integers(1, 9))
+    ldx, ldw = K + int(rng.integers(0, 9)), K + int(rng.integers(0, 9))
+    offx, offw = int(rng.integers(0, 8)), int(rng.integers(0, 8))
+    p = bf16_case(N, K, 6000 + case)
+    xrows = np.zeros((M, ldx), dtype=np.uint16)
+    xrows[:, :K] = p.x[:M]
+    wrows = np.zeros((N, ldw), dtype=np.uint16)
+    wrows[:, :K] = p.w
+    xbuf = np.concatenate([np.zeros(offx, dtype=np.uint16), xrows.ravel()])
+    wbuf = np.concatenate([np.zeros(offw, dtype=np.uint16), wrows.ravel()])
+    xd = bf16_dev(xbuf)[offx:].as_strided((M, K), (ldx, 1))
+    wd = bf16_dev(wbuf)[offw:].as_strided((N, K), (ldw, 1))
+    say(f"bf16 random N={N} K={K} M={M} ldx={ldx} ldw={ldw} offx={offx} offw={offw}")
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_bf16(xd, wd, y)
+    yr, S = _ref(p, M, ldw=ldw, wbuf=wrows, xbuf=xrows, ldx=ldx)
+    assert_accept(y_host(y), yr, S, "f32", f"bf16 random case {case}")
