@@ -5,7 +5,7 @@ Workloads: the int4 decode shapes -- (256 x 1536, block 32, asymmetric, M=1),
 M = 1..8, and the lm_head shape (151936 x 4096, block 32, asymmetric) at M = 1
 and 8 on sampled columns -- plus block sizes 64/256, every output type, ragged
 N, strided and unaligned x, multi-chunk K, a one-hot dequant probe (bit-exact),
-and invariants.
+invariants, and seeded random shapes, block sizes, strides and output types.
 """
 import numpy as np
 import pytest
@@ -364,3 +364,28 @@ def test_uses_current_stream():
     s.synchronize()
     yr, S = int4_ref(256, 1536, 32, True, 101)
     assert_accept(y_host(y), yr[:1], S[:1], "f16", "int4 stream")
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_shapes_and_strides(case):
+    """Seeded random block size, zero points, N, K, M, x row stride and base
+    offset, y row stride and output type: the kernel choices (v_dot2 or
+    matrix cores; whole, split, chunked or phased x) follow from the shape."""
+    rng = np.random.default_rng(7000 + case)
+    bs = [32, 64, 128][int(rng.integers(0, 3))]
+    asym = bool(rng.integers(0, 2))
+    N, M = int(rng.integers(1, 1500)), int(rng.integers(1, 9))
+    K = bs * int(rng.integers(1, 6144 // bs + 1))
+    ldx, offx = K + int(rng.integers(0, 12)), int(rng.integers(0, 3))
+    ldy = N + int(rng.integers(0, 5))
+    out_dtype = [torch.float16, torch.bfloat16, torch.float32][int(rng.integers(0, 3))]
+    p = int4_case(N, K, bs, asym, 7100 + case)
+    xrows = np.zeros((M, ldx), dtype=np.uint16)
+    xrows[:, :K] = p.x[:M]
+    xbuf = np.concatenate([np.zeros(offx, dtype=np.uint16), xrows.ravel()])
+    xd = f16_dev(xbuf)[offx:].as_strided((M, K), (ldx, 1))
+    say(f"int4 random N={N} K={K} bs={bs} asym={asym} M={M} ldx={ldx} offx={offx} ldy={ldy} "
+        f"out={out_dtype}")
+    y = _run(p, M, out_dtype, x=xd, ldy=ldy)
+    yr, S = oracle.int4_gemv(xrows, p.w, p.scales, p.zp, M, N, K, bs, ldx=ldx)
+    assert_accept(y_host(y), yr, S, OUT_NAME[out_dtype], f"int4 random case {case} ({q.last_launch()})")

@@ -4,7 +4,8 @@ Workloads: the 7B-decoder q4_K layer shapes (4096 x 4096), (11008 x 4096),
 (4096 x 11008) at M = 1, direct decode and through the W_dsc plane; M = 1..8
 on smaller shapes; the plane byte-exact against the oracle's plane over a
 matrix of shapes (the page's host-mirror-vs-device test); direct and plane
-paths bitwise equal; a one-hot dequant probe (bit-exact); invariants.
+paths bitwise equal; a one-hot dequant probe (bit-exact); invariants; seeded
+random shapes and strides.
 """
 import numpy as np
 import pytest
@@ -274,3 +275,31 @@ def test_null_plane_is_rejected_on_device():
     with pytest.raises(q.QgemvError) as ei:
         q.qgemv_q4k_dsc(to_dev(p.x[:1]), to_dev(p.w), None, torch.empty((1, 16), device=DEV))
     assert ei.value.status_name == "QG_ERR_NULL_POINTER"
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_shapes_and_strides(case):
+    """Seeded random N, K, M, x row stride and base offset, y row stride:
+    direct decode and the plane (bitwise the same), against the oracle; long
+    rows with many rows of x take row groups."""
+    rng = np.random.default_rng(8000 + case)
+    N, M = int(rng.integers(1, 1500)), int(rng.integers(1, 9))
+    K = 256 * int(rng.integers(1, 49))
+    ldx, offx = K + int(rng.integers(0, 9)), int(rng.integers(0, 4))
+    ldy = N + int(rng.integers(0, 5))
+    p = q4k_case(N, K, 8100 + case)
+    xrows = np.zeros((M, ldx), dtype=np.float32)
+    xrows[:, :K] = p.x[:M]
+    xbuf = np.concatenate([np.zeros(offx, dtype=np.float32), xrows.ravel()])
+    xd = to_dev(xbuf)[offx:].as_strided((M, K), (ldx, 1))
+    wd = to_dev(p.w)
+    say(f"q4k random N={N} K={K} M={M} ldx={ldx} offx={offx} ldy={ldy}")
+    y = torch.full((M, ldy), float("nan"), device=DEV)[:, :N]
+    q.qgemv_q4k(xd, wd, y)
+    what = f"q4k random case {case} ({q.last_launch()})"
+    y2 = torch.full((M, ldy), float("nan"), device=DEV)[:, :N]
+    q.qgemv_q4k_dsc(xd, wd, _plane(wd, N, K), y2)
+    yd = y_host(y)
+    assert np.array_equal(yd, y_host(y2)), what
+    yr, S = oracle.q4k_gemv(xrows, p.w, M, N, K, ldx=ldx)
+    assert_accept(yd, yr, S, "f32", what)
