@@ -240,20 +240,22 @@ def test_invariants():
     q.qgemv_int4_blockwise(f16_dev(p.x[:M]), to_dev(p.w[perm]), f16_dev(p.scales[perm]),
                            to_dev(p.zp[perm]), yp, bs)
     assert np.array_equal(y_host(yp), base[:, perm])
-    # row independence: M >= 2 runs on the matrix cores (v_mfma), M = 1 on
-    # v_dot2; a row of an M = 2 call equals the same row of an M = 3 call
+    # row independence: M >= 3 here runs on the matrix cores (v_mfma), M = 1
+    # and 2 on v_dot2; rows 0..2 of an M = 3 call equal those of an M = 4 call
     # bitwise (same kernel, rows of the MFMA A operand are independent), and
-    # the M = 1 call agrees to the tolerance
+    # the v_dot2 calls agree to the tolerance
     yr, S = int4_ref(N, K, bs, True, 91)
     outs = {}
-    for MM in (1, 2, 3):
+    for MM in (1, 2, 3, 4):
         yy = torch.empty((MM, N), dtype=torch.float32, device=DEV)
         q.qgemv_int4_blockwise(f16_dev(p.x[4:4 + MM]), to_dev(p.w), f16_dev(p.scales),
                                to_dev(p.zp), yy, bs)
+        assert ("int4_mfma_" in q.last_launch()) == (MM >= 3), q.last_launch()
         outs[MM] = y_host(yy)
-    assert np.array_equal(outs[2], outs[3][:2])
+    assert np.array_equal(outs[3], outs[4][:3])
     assert_accept(outs[1], yr[4:5], S[4:5], "f32", "row 4, M=1")
-    assert_accept(outs[3], yr[4:7], S[4:7], "f32", "rows 4..6, M=3")
+    assert_accept(outs[2], yr[4:6], S[4:6], "f32", "rows 4..5, M=2")
+    assert_accept(outs[4], yr[4:8], S[4:8], "f32", "rows 4..7, M=4")
     assert_accept(base, yr[:M], S[:M], "f32", "M=8")
 
 
@@ -285,7 +287,8 @@ def test_one_hot_probe_matrix_core_path_is_bit_exact(K, bs):
         assert np.array_equal(got.view(np.uint32)[nz], want.view(np.uint32)[nz]), kk
 
 
-@pytest.mark.parametrize("bs,asym,M", [(64, True, 4), (128, False, 5), (256, True, 8), (32, True, 2)])
+@pytest.mark.parametrize("bs,asym,M", [(64, True, 4), (128, False, 5), (256, True, 8), (32, True, 2),
+                                       (32, True, 3)])
 def test_wide_matrix_sampled(bs, asym, M):
     # 65576 rows = 4099 tiles of 16: enough for every wave to own whole tiles
     N, K = 65576, 1024
