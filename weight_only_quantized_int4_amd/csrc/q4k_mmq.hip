@@ -23,9 +23,14 @@
 // 32g+8j..+8 for both chunks, and the A operand takes the activations of the
 // same k.  A wavefront owns 16 activation rows x 64 weight rows (1 x 4 MFMA
 // blocks); a workgroup of 4 x 2 wavefronts covers 64 activation rows x 128
-// weight rows, stages one super-block (256 k) of its codes, quant bytes,
-// plane entries and activation scales in LDS and prefetches the next
-// super-block into registers meanwhile.  The rescale runs in fp32 per chunk.
+// weight rows, stages one super-block (256 k) of its codes, quant bytes (split
+// into low and high nibbles on the way into LDS), plane entries and activation
+// scales in LDS and prefetches the next super-block into registers meanwhile.
+// The dv term is rescaled in fp32 per chunk and output on the vector ALUs; the
+// mv term, a product over chunks of (d_a * sum q_a) and mv, runs on the fp32
+// matrix cores (v_mfma_f32_16x16x4f32, four chunks per instruction) into
+// accumulators of its own, added at the end.  Vector-ALU issue is the limit of
+// this kernel; both moves take work off it (measured 3-11% faster each).
 #include "qgemv_device.h"
 #include "qgemv_launch.h"
 
@@ -88,7 +93,7 @@ constexpr int kWaveRows = 64;      // weight rows per wavefront (4 MFMA blocks)
 constexpr int kRowWaves = 2;       // wavefronts along the weight rows
 constexpr int kBN = kWaveRows * kRowWaves;  // weight rows per workgroup
 constexpr int kAStride = 256 + 16;  // LDS bytes per staged activation row (one super-block)
-constexpr int kBStride = 128 + 16;  // LDS bytes per staged weight row (its 128 quant bytes)
+constexpr int kBStride = 256 + 16;  // LDS bytes per staged weight row (128 low, 128 high nibbles)
 
 // WT wavefronts along the activation rows, each with TB blocks of 16 rows.
 template <int WT, int TB>
@@ -171,10 +176,14 @@ __global__ __launch_bounds__((MmqShape<WT, TB>::kThreads)) void q4k_mmq_kernel(
       const int p = tid + i * S::kThreads;
       *reinterpret_cast<u32x4*>(As + (p >> 4) * kAStride + (p & 15) * 16) = ra[i];
     }
+    // the quant bytes split once per super-block into their low nibbles
+    // (chunks 2g) and high nibbles (chunks 2g+1), one byte per 4-bit value
 #pragma unroll
     for (int i = 0; i < S::kBPieces; ++i) {
       const int p = tid + i * S::kThreads;
-      *reinterpret_cast<u32x4*>(Bs + (p >> 3) * kBStride + (p & 7) * 16) = rb[i];
+      char* dst = Bs + (p >> 3) * kBStride + (p & 7) * 16;
+      *reinterpret_cast<u32x4*>(dst) = rb[i] & 0x0F0F0F0Fu;
+      *reinterpret_cast<u32x4*>(dst + 128) = (rb[i] >> 4) & 0x0F0F0F0Fu;
     }
 #pragma unroll
     for (int i = 0; i < S::kPEntries; ++i) Ps[tid + i * S::kThreads] = rp[i];
@@ -189,11 +198,14 @@ __global__ __launch_bounds__((MmqShape<WT, TB>::kThreads)) void q4k_mmq_kernel(
     }
   };
 
-  f32x4 acc[TB][4];
+  f32x4 acc[TB][4], accm[TB][4];
 #pragma unroll
   for (int a = 0; a < TB; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4; ++b) {
+      acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accm[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   const i32x4 zero = {0, 0, 0, 0};
 
   // LDS byte offsets of this lane's operands
@@ -208,12 +220,25 @@ __global__ __launch_bounds__((MmqShape<WT, TB>::kThreads)) void q4k_mmq_kernel(
 #pragma unroll 1
   for (int sb = 0; sb < nsb; ++sb) {
     fetch(sb + 1 < nsb ? sb + 1 : sb);  // unconditional: the last round re-reads its own
+    // mv term: sum over the super-block's chunks c of (d_a * sum q_a)[t, c] *
+    // mv[n, c], four chunks per fp32 MFMA (A[t][k] = chunk 4hh+k of token t,
+    // B[k][n] = the same chunk of weight row n), accumulated apart from the
+    // integer products' rescale
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int c = 4 * hh + g;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const float am = Ss[c * S::kBT + wt * S::kWaveTokens + tb * 16 + n16].y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float bm = Ps[c * kBN + p_row0 + r * 16].y;
+          accm[tb][r] = __builtin_amdgcn_mfma_f32_16x16x4f32(am, bm, accm[tb][r], 0, 0, 0);
+        }
+      }
+    }
 #pragma unroll 1
     for (int pair = 0; pair < 4; ++pair) {
-      uint64_t braw[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        braw[r] = *reinterpret_cast<const uint64_t*>(Bs + b_off0 + r * 16 * kBStride + pair * 32);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int cc = pair * 2 + h;
@@ -224,7 +249,7 @@ __global__ __launch_bounds__((MmqShape<WT, TB>::kThreads)) void q4k_mmq_kernel(
         int64_t bv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          bv[r] = (int64_t)((h ? (braw[r] >> 4) : braw[r]) & 0x0F0F0F0F0F0F0F0Full);
+          bv[r] = *reinterpret_cast<const int64_t*>(Bs + b_off0 + r * 16 * kBStride + h * 128 + pair * 32);
         i32x4 dd[TB][4];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
@@ -239,17 +264,11 @@ __global__ __launch_bounds__((MmqShape<WT, TB>::kThreads)) void q4k_mmq_kernel(
           const float4* sp = reinterpret_cast<const float4*>(Ss + cc * S::kBT + s_tok0 + tb * 16);
           const float4 s01 = sp[0], s23 = sp[1];
           const float da[4] = {s01.x, s01.z, s23.x, s23.z};
-          const float sa[4] = {s01.y, s01.w, s23.y, s23.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float f = (float)dd[tb][r][i];
-              float a = acc[tb][r][i];
-              a = __builtin_fmaf(da[i] * pc[r].x, f, a);
-              a = __builtin_fmaf(pc[r].y, sa[i], a);
-              acc[tb][r][i] = a;
-            }
+            for (int i = 0; i < 4; ++i)
+              acc[tb][r][i] = __builtin_fmaf(da[i] * pc[r].x, (float)dd[tb][r][i], acc[tb][r][i]);
         }
         // keep the next chunk's operands and products from being hoisted here
         __builtin_amdgcn_sched_barrier(0);
@@ -271,7 +290,7 @@ __global__ __launch_bounds__((MmqShape<WT, TB>::kThreads)) void q4k_mmq_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = t0 + wt * S::kWaveTokens + tb * 16 + 4 * g + i;
-        if (tok < T && row < N) y[(int64_t)tok * ldy + row] = acc[tb][r][i];
+        if (tok < T && row < N) y[(int64_t)tok * ldy + row] = acc[tb][r][i] + accm[tb][r][i];
       }
     }
 }
@@ -314,7 +333,7 @@ hipError_t launch_q4k_mmq(const int8_t* qa, const float* sda, const uint8_t* w, 
   // One block of 16 activation rows per wavefront (TB = 1) and 4 wavefronts
   // along the activation rows measured fastest for T = 8 .. 2048 on the 7B
   // layer shapes (against 2 blocks per wavefront and 2 wavefronts: twice the
-  // wavefronts for the same work, 111 instead of 157-184 VGPRs, and the stalls
+  // wavefronts for the same work, ~115 instead of 157-184 VGPRs, and the stalls
   // of one wavefront overlap another's; 4096 x 4096 at T = 512: 81 -> 61 us).
   return launch_mmq_wt<4, 1>(qa, s2, w, p2, y, ldy, T, N, K, stream);
 }
