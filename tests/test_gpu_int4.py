@@ -301,6 +301,21 @@ def test_wide_matrix_sampled(bs, asym, M):
     assert_accept(y[:, list(cols)], yr[:M], S[:M], "f32", f"int4 wide bs={bs} M={M}")
 
 
+@pytest.mark.parametrize("N,K,bs,mfma", [(4096, 4096, 128, True), (4100, 11008, 32, True),
+                                         (2064, 4096, 64, True), (4096, 4096, 32, False),
+                                         (1536, 6912, 128, False), (2048, 1536, 64, False)])
+def test_two_rows_kernel_choice(N, K, bs, mfma):
+    """M = 2 runs on the matrix cores except with blocks of 32 along rows of at
+    most 4096 weights, or on matrices of at most 2048 rows (v_dot2); both
+    kernels meet the tolerance on every column."""
+    say(f"int4 M=2 N={N} K={K} bs={bs} mfma={mfma}")
+    p = int4_case(N, K, bs, True, 740 + bs)
+    y = y_host(_run(p, 2, torch.float32))
+    assert ("int4_mfma_" in q.last_launch()) == mfma, q.last_launch()
+    yr, S = int4_ref(N, K, bs, True, 740 + bs)
+    assert_accept(y, yr[:2], S[:2], "f32", f"int4 M=2 {N}x{K} bs={bs}")
+
+
 @pytest.mark.parametrize("N,K,bs,asym", [(4096, 11008, 32, False), (4100, 14336, 32, True),
                                          (4096, 4096, 128, True), (11008, 4096, 128, False),
                                          (6912, 1536, 64, True)])

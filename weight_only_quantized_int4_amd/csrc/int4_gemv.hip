@@ -887,13 +887,16 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
     const uintptr_t salign = block_size >= 128 ? 2 : (size_t)8 * 32 / block_size;
     const bool aligned = (reinterpret_cast<uintptr_t>(scales) % salign == 0) &&
                          (block_size != 32 || reinterpret_cast<uintptr_t>(zp) % 2 == 0);
-    // Two rows of x with blocks of 32 along rows of at most 4096 weights stay
-    // on v_dot2: the matrix-core kernel's per-block scaling and lane swaps
-    // cost more there than v_dot2 spends on a second row (measured cold, in
-    // us, v_dot2 / matrix cores: 4096 x 4096 6.0 / 6.8, 14336 x 4096 11.7 /
-    // 12.4, 32000 x 4096 18.7 / 19.8, 11008 x 4096 10.1 / 10.4; with 11008
-    // or 14336 weights per row, or blocks of 128, the matrix cores win).
-    const bool dot2_pair = M == 2 && block_size == 32 && K <= 4096;
+    // Two rows of x stay on v_dot2 (measured cold, in us, v_dot2 / matrix
+    // cores) with blocks of 32 along rows of at most 4096 weights, where the
+    // matrix-core kernel's per-block scaling and lane swaps cost more than
+    // v_dot2 spends on a second row (4096 x 4096 6.0 / 6.8, 14336 x 4096
+    // 11.7 / 12.4, 32000 x 4096 18.7 / 19.8, 11008 x 4096 10.1 / 10.4), and
+    // on matrices of at most 2048 rows, whose few 16-row tiles the
+    // matrix-core kernel spreads less well (1536 x 6912: blocks of 64 6.5 /
+    // 8.0, blocks of 128 6.4 / 7.1).  With longer rows, or blocks of 64 or
+    // more on taller matrices, the matrix cores win.
+    const bool dot2_pair = M == 2 && ((block_size == 32 && K <= 4096) || N <= 2048);
     if (K % 128 == 0 && aligned && !dot2_pair &&
         ((size_t)M * K * 2 <= (size_t)kLdsMax || mfma_chunk_items(M, K) != 0))
       return launch_mfma<M>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
