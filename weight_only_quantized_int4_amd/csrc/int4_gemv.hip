@@ -385,7 +385,8 @@ __global__ __launch_bounds__(NT) void int4_gemv_persistent(
   }
 }
 
-// Matrix-core variant for M >= 2 (where the v_dot2 path turns VALU-bound):
+// Matrix-core variant for M >= 2 (where the v_dot2 path turns VALU-bound;
+// the launcher keeps some M = 2 shapes on v_dot2, where it measured faster):
 // v_mfma_f32_16x16x32_f16 with x as the A operand and 16 weight rows as the B
 // operand, so one MFMA contracts 32 k for 16 rows.  A rows M..15 repeat real
 // rows (their D rows are never stored), so every A read is unconditional.
