@@ -226,6 +226,21 @@ def test_binding_raises_with_library_message():
     assert ei.value.status == QG_ERR_NULL_POINTER
 
 
+def test_binding_refuses_wrong_dtypes_before_the_call():
+    w = torch.zeros(4, 144, dtype=torch.uint8)
+    with pytest.raises(TypeError, match="x: expected torch.float32"):
+        q.qgemv_q4k(torch.zeros(1, 256, dtype=torch.float16), w, torch.zeros(1, 4), stream=0)
+    with pytest.raises(TypeError, match="w: expected torch.uint8"):
+        q.qgemv_q4k(torch.zeros(1, 256), w.view(torch.int8), torch.zeros(1, 4), stream=0)
+    with pytest.raises(TypeError, match="y: expected"):
+        q.gemv_bf16(torch.zeros(1, 8, dtype=torch.bfloat16), torch.zeros(4, 8, dtype=torch.bfloat16),
+                    torch.zeros(1, 4, dtype=torch.float64), stream=0)
+    with pytest.raises(TypeError, match="scales: expected torch.float16"):
+        q.qgemv_int4_blockwise(torch.zeros(1, 64, dtype=torch.float16), torch.zeros(4, 32, dtype=torch.uint8),
+                               torch.zeros(4, 2), None, torch.zeros(1, 4, dtype=torch.float16), 32,
+                               stream=0)
+
+
 def test_product_package_does_not_import_the_oracle():
     pkg = os.path.join(ROOT, "weight_only_quantized_int4_amd")
     for dirpath, _, files in os.walk(pkg):

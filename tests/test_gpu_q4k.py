@@ -269,6 +269,16 @@ def test_invariants():
     assert np.all(y_host(y) == 0.0)
 
 
+def test_host_tensor_is_refused_before_the_call():
+    # a host tensor's address must never reach a kernel: the binding refuses it
+    p = q4k_case(16, 256, 1)
+    say("q4k host tensor refused")
+    with pytest.raises(ValueError, match="x must be a GPU tensor"):
+        q.qgemv_q4k(torch.from_numpy(p.x[:1]), to_dev(p.w), torch.empty((1, 16), device=DEV))
+    with pytest.raises(ValueError, match="y must be a GPU tensor"):
+        q.qgemv_q4k(to_dev(p.x[:1]), to_dev(p.w), torch.empty((1, 16)))
+
+
 def test_null_plane_is_rejected_on_device():
     p = q4k_case(16, 256, 1)
     say("q4k null plane")

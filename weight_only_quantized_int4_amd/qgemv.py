@@ -1,10 +1,11 @@
 """ctypes binding of libqgemv.so -- argument marshalling only.
 
-Every function takes torch tensors, checks nothing that the C library does not
-check itself beyond what ctypes needs (dtype -> pointer type, shapes -> sizes,
-strides -> leading dimensions), passes ``data_ptr()`` and the current HIP
-stream, and raises ``QgemvError`` with the library's own message on a non-OK
-status.  All compute happens in the HIP kernels; if the library is missing the
+Every function takes torch tensors and checks only what the C library cannot
+see through a raw pointer: each tensor's dtype, and that it lives in GPU
+memory (on a machine with a GPU, a host tensor's address would otherwise reach
+a kernel).  It turns shapes into sizes and strides into leading dimensions,
+passes ``data_ptr()`` and the current HIP stream, and raises ``QgemvError``
+with the library's own message on a non-OK status.  All compute happens in the HIP kernels; if the library is missing the
 import of a function fails loudly -- there is no CPU fallback.
 """
 from __future__ import annotations
@@ -85,6 +86,28 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+_F16, _BF16, _F32, _U8, _I8 = (torch.float16,), (torch.bfloat16,), (torch.float32,), (torch.uint8,), \
+    (torch.int8,)
+_OUT = tuple(_OUT_TYPES)
+_gpu_present: Optional[bool] = None
+
+
+def _arg(t: Optional[torch.Tensor], name: str, dtypes) -> None:
+    """Refuse a tensor of another dtype, or one in host memory on a machine
+    with a GPU.  None passes through: the library reports a missing required
+    pointer itself."""
+    global _gpu_present
+    if t is None:
+        return
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: expected {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if t.device.type != "cuda":
+        if _gpu_present is None:
+            _gpu_present = torch.cuda.is_available()
+        if _gpu_present:
+            raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -103,6 +126,9 @@ def qgemv_int4_blockwise(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
                          block_size: int, stream=None) -> torch.Tensor:
     """y[M,N] = x[M,K] . dequant(w)^T.  x fp16 [M,K]; w uint8 [N,K/2]; scales
     fp16 [N,K/bs]; zero_points uint8 [N,ceil(K/bs/2)] or None; y fp16/bf16/fp32 [M,N]."""
+    for t, n, d in ((x, "x", _F16), (w, "w", _U8), (scales, "scales", _F16),
+                    (zero_points, "zero_points", _U8), (y, "y", _OUT)):
+        _arg(t, n, d)
     M, K = x.shape
     N = w.shape[0]
     _check("qgemv_int4_blockwise", load_library().qgemv_int4_blockwise(
@@ -113,6 +139,8 @@ def qgemv_int4_blockwise(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
 
 def qgemv_q4k(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
     """q4_K GEMV.  x fp32 [M,K]; w uint8 [N, K/256*144]; y fp32 [M,N]."""
+    for t, n, d in ((x, "x", _F32), (w, "w", _U8), (y, "y", _F32)):
+        _arg(t, n, d)
     M, K = x.shape
     N = w.shape[0]
     _check("qgemv_q4k", load_library().qgemv_q4k(
@@ -123,6 +151,8 @@ def qgemv_q4k(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=None) ->
 def qgemv_q4k_dsc(x: torch.Tensor, w: torch.Tensor, dsc: Optional[torch.Tensor],
                   y: torch.Tensor, stream=None) -> torch.Tensor:
     """q4_K GEMV with (dv, mv) read from the W_dsc plane (fp32 [(K/32)*N, 2])."""
+    for t, n, d in ((x, "x", _F32), (w, "w", _U8), (dsc, "dsc", _F32), (y, "y", _F32)):
+        _arg(t, n, d)
     M, K = x.shape
     N = w.shape[0]
     _check("qgemv_q4k_dsc", load_library().qgemv_q4k_dsc(
@@ -132,6 +162,8 @@ def qgemv_q4k_dsc(x: torch.Tensor, w: torch.Tensor, dsc: Optional[torch.Tensor],
 
 def gemv_bf16(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
     """y[M,N] = x[M,K] . w[N,K]^T in bf16 (any K, any 2-byte offset)."""
+    for t, n, d in ((x, "x", _BF16), (w, "w", _BF16), (y, "y", _OUT)):
+        _arg(t, n, d)
     M, K = x.shape
     N = w.shape[0]
     _check("gemv_bf16", load_library().gemv_bf16(
@@ -147,6 +179,8 @@ def q4k_dsc_plane_bytes(N: int, K: int) -> int:
 def q4k_build_dsc_plane(w: torch.Tensor, dsc_out: torch.Tensor, N: int, K: int,
                         stream=None) -> torch.Tensor:
     """Load-time repack of raw q4_K weights into the chunk-major W_dsc plane."""
+    _arg(w, "w", _U8)
+    _arg(dsc_out, "dsc_out", _F32)
     _check("q4k_build_dsc_plane", load_library().q4k_build_dsc_plane(
         _ptr(w), _ptr(dsc_out), N, K, _stream(stream)))
     return dsc_out
@@ -158,6 +192,8 @@ def q4k_mmq_workspace_bytes(T: int, K: int) -> int:
 
 def q8_quantize_rows(x: torch.Tensor, qa: torch.Tensor, sda: torch.Tensor, stream=None):
     """8-bit activation prepass.  x fp32 [T,K]; qa int8 [T,K]; sda fp32 [T,K/32,2]."""
+    for t, n, d in ((x, "x", _F32), (qa, "qa", _I8), (sda, "sda", _F32)):
+        _arg(t, n, d)
     T, K = x.shape
     _check("q8_quantize_rows", load_library().q8_quantize_rows(
         _ptr(x), _ld(x), _ptr(qa), _ptr(sda), T, K, _stream(stream)))
@@ -168,6 +204,9 @@ def qgemm_q4k_mmq(x: torch.Tensor, w: torch.Tensor, dsc: Optional[torch.Tensor],
                   workspace: torch.Tensor, stream=None) -> torch.Tensor:
     """q4_K prefill: y[T,N] fp32 from x fp32 [T,K], raw q4_K w, its W_dsc plane
     and a caller-owned workspace (uint8, >= q4k_mmq_workspace_bytes(T, K))."""
+    for t, n, d in ((x, "x", _F32), (w, "w", _U8), (dsc, "dsc", _F32), (y, "y", _F32),
+                    (workspace, "workspace", None)):
+        _arg(t, n, d)
     T, K = x.shape
     N = w.shape[0]
     _check("qgemm_q4k_mmq", load_library().qgemm_q4k_mmq(
