@@ -161,8 +161,10 @@ def q4k_linear(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = Non
         label = LABEL_PLANE
     elif failure is not None:
         label = LABEL_FALLBACK
-        if not _warned:
+        with _lock:
+            first = not _warned
             _warned = True
+        if first:
             warnings.warn(f"q4_K plane unavailable ({failure}); falling back to in-kernel "
                           f"decode (this warning is shown once per process)", RuntimeWarning,
                           stacklevel=2)
@@ -219,7 +221,7 @@ def reset_liveness() -> None:
     with _lock:
         for k in _liveness:
             _liveness[k] = 0
-    _warned = False
+        _warned = False
 
 
 def explain() -> str:
