@@ -66,7 +66,7 @@ def test_prepass_bit_exact(T, K, ldx, offset):
 
 
 @pytest.mark.parametrize("T,N,K", [(1, 64, 256), (37, 300, 512), (130, 1000, 1024), (64, 129, 2048),
-                                   (257, 256, 256)])
+                                   (257, 256, 256), (1, 1, 256), (65, 1, 512), (2048, 130, 256)])
 def test_full_shapes(T, N, K):
     p = q4k_case(N, K, 910 + N)
     x = datagen.prefill_x(T, K, 911 + T)
