@@ -46,6 +46,15 @@ MUTANTS = {
                                                      "double term_m = (double)mv * (double)sum;"),
     "mmq chunk coefficients": ("oracle_q4k_coeffs(w, K, n, c, &dv, &mv); /* chunk c of row n */",
                                "oracle_q4k_coeffs(w, K, n, c / 2, &dv, &mv);"),
+    "f32 rounding one significand bit short": (
+        "double oracle_round_f32(double v) { return round_to_format(v, 24, -126, 0x1.FFFFFEp127); }",
+        "double oracle_round_f32(double v) { return round_to_format(v, 23, -126, 0x1.FFFFFEp127); }"),
+    "f32 rounding subnormal edge": (
+        "double oracle_round_f32(double v) { return round_to_format(v, 24, -126, 0x1.FFFFFEp127); }",
+        "double oracle_round_f32(double v) { return round_to_format(v, 24, -125, 0x1.FFFFFEp127); }"),
+    "f32 rounding without overflow": (
+        "double oracle_round_f32(double v) { return round_to_format(v, 24, -126, 0x1.FFFFFEp127); }",
+        "double oracle_round_f32(double v) { return round_to_format(v, 24, -126, 0x1.FFFFFEp128); }"),
     "mmq activation index": ("dot += (int64_t)qw[k] * (int64_t)qa[t * K + k];",
                              "dot += (int64_t)qw[k] * (int64_t)qa[k];"),
 }

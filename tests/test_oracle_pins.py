@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import datagen
 import oracle
 from oracle import numpy_cross as npx
 
@@ -74,6 +75,30 @@ def test_round_bf16_matches_torch(oracle_lib):
     want = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
     for v, w in zip(vals, want):
         assert oracle.round_to(float(v), "bf16") == w, v
+
+
+def test_round_f32_matches_numpy(oracle_lib):
+    """binary32 rounding against NumPy's float64 -> float32 cast (IEEE
+    round-to-nearest-even): random values over the whole range, exact ties
+    between neighbouring normal and subnormal values (even neighbour wins),
+    the subnormal and overflow edges, and signed zeros."""
+    rng = np.random.default_rng(9)
+    rand = rng.standard_normal(6000) * 10.0 ** rng.integers(-46, 39, 6000)
+    i = np.arange(0, 600, dtype=np.float64)
+    ties_normal = np.concatenate([(2.0 ** 23 + i + 0.5) * 2.0 ** (e - 23) for e in (-126, -3, 0, 77)])
+    ties_sub = (i + 0.5) * 2.0 ** -149
+    tiny = np.array([2.0 ** -150, 3 * 2.0 ** -151, 2.0 ** -149, 2.0 ** -126 * (1 - 2.0 ** -25),
+                     1e-46, 1e-45])
+    maxf = float(np.finfo(np.float32).max)
+    big = np.array([maxf, maxf + 2.0 ** 103, maxf + 2.0 ** 103 - 2.0 ** 60, 2.0 ** 128, 1e39,
+                    3.4e38])
+    vals = np.concatenate([rand, ties_normal, ties_sub, tiny, big, [0.0, -0.0]])
+    vals = np.concatenate([vals, -vals])
+    with np.errstate(over="ignore"):
+        want_all = vals.astype(np.float32).astype(np.float64)
+    for v, want in zip(vals, want_all):
+        got = oracle.round_to(float(v), "f32")
+        assert got == want and np.signbit(got) == np.signbit(want), (v, got, want)
 
 
 def test_ulp_values(oracle_lib):
@@ -347,6 +372,39 @@ def test_invariants_zero_weights(oracle_lib):
     wq = wq.reshape(3, 288)
     y, _ = oracle.q4k_gemv(q.x, wq, 8, 3, 512)
     assert np.all(y == 0.0)
+
+
+def test_q4k_exactly_zero_weights(oracle_lib):
+    """q4_K weights that are exactly zero with nonzero coefficients: every
+    chunk has quant q, scale sc and min m = sc*q with d = dmin, so
+    w = d*sc*q - d*m = 0 exactly.  The definition gives y = 0 and S = 0; with
+    some chunks random instead, the zero chunks add nothing."""
+    from q4k_cases import pack_scale_min, zero_weight_rows
+
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        sc, m = rng.integers(0, 64, 8), rng.integers(0, 64, 8)
+        packed = pack_scale_min(sc, m)
+        for cc in range(8):
+            assert oracle.q4k_scale_min(packed, cc) == (sc[cc], m[cc])
+    N, K = 6, 512
+    w = zero_weight_rows(N, K, seed=12)
+    assert np.all(oracle.q4k_dequant(w, N, K) == 0.0)
+    x = rng.standard_normal((3, K)).astype(np.float32)
+    y, S = oracle.q4k_gemv(x, w, 3, N, K)
+    assert np.all(y == 0.0) and np.all(S == 0.0)
+    plane = oracle.q4k_build_plane(w, N, K)
+    assert np.all(plane[:, 0] > 0.0) and np.all(plane[:, 1] < 0.0)
+    y2, S2 = oracle.q4k_plane_gemv(x, w, plane, 3, N, K)
+    assert np.all(y2 == 0.0) and np.all(S2 == 0.0)
+    # half of the chunks random: the degenerate ones contribute nothing
+    wm = zero_weight_rows(N, K, seed=13, zero_frac=[0.5] * N)
+    dq = oracle.q4k_dequant(wm, N, K).reshape(N, K // 32, 32)
+    zero_chunks = np.all(dq == 0.0, axis=2)
+    assert 0 < zero_chunks.sum() < zero_chunks.size
+    ym, Sm = oracle.q4k_gemv(x, wm, 3, N, K)
+    keep = np.repeat(~zero_chunks, 32, axis=1)
+    assert np.allclose(ym, (x.astype(np.float64) @ (dq.reshape(N, K) * keep).T), rtol=1e-12, atol=0)
 
 
 def test_invariants_sign_and_scale(oracle_lib):
