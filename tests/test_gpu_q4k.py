@@ -104,8 +104,8 @@ def test_m1_rows_and_pieces_per_lane(N, K):
 
 @pytest.mark.parametrize("M", [2, 3])
 def test_long_rows_x_resident(M):
-    # K = 11008: x and its chunk sums take 94 KB (M = 2) and 141 KB (M = 3) of
-    # LDS, so the whole of x stays resident in one workgroup
+    # K = 11008: x takes 94 KB (M = 2) and 140 KB (M = 3) of LDS, so the
+    # whole of x stays resident in one workgroup
     N, K = 700, 11008
     p = q4k_case(N, K, 422)
     yr, S = q4k_ref(N, K, 422)
@@ -136,7 +136,7 @@ def test_row_groups_and_strided_x():
 
 @pytest.mark.parametrize("M", [1, 2, 8])
 def test_multi_chunk_k(M):
-    # K = 40960: one row of x and its chunk sums exceed 160 KB, so x is staged
+    # K = 40960: one row of x exceeds 160 KB of LDS, so x is staged
     # in LDS one K chunk (a whole number of super-blocks) at a time, for at
     # most 4 rows of x per launch
     N, K = 64, 40960
@@ -313,3 +313,35 @@ def test_random_shapes_and_strides(case):
     assert np.array_equal(yd, y_host(y2)), what
     yr, S = oracle.q4k_gemv(xrows, p.w, M, N, K, ldx=ldx)
     assert_accept(yd, yr, S, "f32", what)
+
+
+@pytest.mark.parametrize("N,K", [(64, 2048), (300, 11008)])
+@pytest.mark.parametrize("M", [1, 8])
+def test_exactly_zero_weight_rows(N, K, M):
+    """Rows whose weights are all exactly zero although no chunk's (dv, mv)
+    is: y must be exactly 0 there (the bound is 1 subnormal ulp), through the
+    header and through the plane.  The second half of the rows mixes such
+    chunks with random ones and is held to the usual bound.  K = 11008 at
+    M = 8 runs as row groups of x."""
+    from q4k_cases import zero_weight_rows
+
+    half = N // 2
+    w = zero_weight_rows(N, K, seed=4000 + K, zero_frac=[1.0] * half + [0.5] * (N - half))
+    x = np.random.default_rng(4100 + M).standard_normal((M, K)).astype(np.float32)
+    yr, S = oracle.q4k_gemv(x, w, M, N, K)
+    assert np.all(S[:, :half] == 0.0) and np.all(S[:, half:] > 0.0)
+    xd, wd = to_dev(x), to_dev(w)
+    dsc = _plane(wd, N, K)
+    outs = []
+    for use_plane in (False, True):
+        say(f"q4k zero-weight rows N={N} K={K} M={M} plane={use_plane}")
+        y = torch.full((M, N), float("nan"), device=DEV)
+        if use_plane:
+            q.qgemv_q4k_dsc(xd, wd, dsc, y)
+        else:
+            q.qgemv_q4k(xd, wd, y)
+        got = y_host(y)
+        outs.append(got)
+        assert np.all(got[:, :half] == 0.0), (use_plane, np.abs(got[:, :half]).max())
+        assert_accept(got, yr, S, "f32", f"q4k zero rows {N}x{K} M={M} plane={use_plane}")
+    assert np.array_equal(outs[0].view(np.uint64), outs[1].view(np.uint64))

@@ -21,11 +21,12 @@
 //    loop-invariant and branch-free.  A K = 4096 row is 64 pieces, one per
 //    lane, so every lane's 48 bytes are in flight at once; a workgroup of 16
 //    wavefronts covers 16 rows and shares one staged copy of x.
-//  * Rank-1 factorisation per chunk: sum_l (dv*q_l + mv) x_l is evaluated as
-//    dv * (sum_l q_l x_l) + mv * (sum_l x_l).  The chunk sums of x are computed
-//    once per workgroup while x is staged in LDS, so the inner loop spends one
-//    fp32 FMA per weight (v_fma_mix_f32 on an exact fp16 quant).  With a one-hot
-//    x this still reproduces w = RN(dv*q + mv) bit-exactly.
+//  * Every weight is dequantized on its own, w = RN(dv*q + mv) (one
+//    v_fma_mix_f32 on the exact fp16 quant), and then multiplied with x in
+//    fp32.  This is the definition itself, so a one-hot x reproduces w
+//    bit-exactly and weights that are exactly zero contribute exactly zero
+//    (the factored form dv*sum(q*x) + mv*sum(x) would leave a rounding
+//    residue of two large partial sums there, outside the error bound).
 //  * Quants are converted with the fp16 1024.0 mantissa trick (exact), as in
 //    the int4 kernel.
 //  * Weights are read with plain (cached) loads: a super-block's header and
@@ -75,6 +76,78 @@ struct Q4kPiece {
   float2 ea, eb;  // plane entries of chunks 2g and 2g+1 (DSC = true)
 };
 
+// (dv, mv) of the piece's two chunks 2g and 2g+1: from the plane, or decoded
+// from the header with one binary32 multiply each and an exact negation (the
+// same operations that build the plane, so both paths see the same values).
+template <bool DSC>
+__device__ __forceinline__ void piece_coeffs(const Q4kPiece& cur, int g, float& dva, float& mva,
+                                             float& dvb, float& mvb) {
+  if constexpr (DSC) {
+    dva = cur.ea.x; mva = cur.ea.y; dvb = cur.eb.x; mvb = cur.eb.y;
+  } else {
+    uint32_t s2, m2;
+    scale_min_pair(cur.h.y, cur.h.z, cur.h.w, g, s2, m2);
+    const float d = f16_to_f32(cur.h.x & 0xFFFFu);
+    const float dmin = f16_to_f32(cur.h.x >> 16);
+    dva = d * (float)(s2 & 0xFFu);
+    dvb = d * (float)(s2 >> 8);
+    mva = -(dmin * (float)(m2 & 0xFFu));
+    mvb = -(dmin * (float)(m2 >> 8));
+  }
+}
+
+// acc[m] += sum over the piece's 64 weights of w * x[m, k].  xa points at the
+// staged x of chunk 2g (row stride XSTR floats; chunk 2g+1 follows at +32).
+// Word t of the 32 quant bytes holds bytes 4t..4t+3: their low nibbles are
+// elements 4t..4t+3 of chunk 2g, their high nibbles those of chunk 2g+1.
+// Each weight is w = RN(dv*q + mv) (v_fma_mix_f32 on the exact fp16 quant);
+// the two chunks accumulate into separate registers (two dependency chains).
+template <int M>
+__device__ __forceinline__ void piece_mac(const Q4kPiece& cur, const float* xa, int XSTR,
+                                          float dva, float mva, float dvb, float mvb,
+                                          uint32_t magic, float (&acc_a)[M], float (&acc_b)[M]) {
+  const f16x2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const f16x2 m64 = {(_Float16)-64.0f, (_Float16)-64.0f};
+  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t word = t < 4 ? word_of(cur.q0, t) : word_of(cur.q1, t - 4);
+    const uint32_t w8 = word >> 8;
+    // exact fp16 quants: A = elements (4t, 4t+2) and C = (4t+1, 4t+3) of
+    // chunk 2g; B and D the same elements of chunk 2g+1
+    const f16x2 A = bitcast<f16x2>((word & 0x000F000Fu) | magic) + m1024;
+    const f16x2 C = bitcast<f16x2>((w8 & 0x000F000Fu) | magic) + m1024;
+    const f16x2 B =
+        __builtin_elementwise_fma(bitcast<f16x2>((word & 0x00F000F0u) | magic), sixteenth, m64);
+    const f16x2 D =
+        __builtin_elementwise_fma(bitcast<f16x2>((w8 & 0x00F000F0u) | magic), sixteenth, m64);
+    const float wa0 = __builtin_fmaf((float)A.x, dva, mva);
+    const float wa1 = __builtin_fmaf((float)C.x, dva, mva);
+    const float wa2 = __builtin_fmaf((float)A.y, dva, mva);
+    const float wa3 = __builtin_fmaf((float)C.y, dva, mva);
+    const float wb0 = __builtin_fmaf((float)B.x, dvb, mvb);
+    const float wb1 = __builtin_fmaf((float)D.x, dvb, mvb);
+    const float wb2 = __builtin_fmaf((float)B.y, dvb, mvb);
+    const float wb3 = __builtin_fmaf((float)D.y, dvb, mvb);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float4 xa4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 4 * t);
+      const float4 xb4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 32 + 4 * t);
+      float u = acc_a[m], v = acc_b[m];
+      u = __builtin_fmaf(wa0, xa4.x, u);
+      u = __builtin_fmaf(wa1, xa4.y, u);
+      u = __builtin_fmaf(wa2, xa4.z, u);
+      u = __builtin_fmaf(wa3, xa4.w, u);
+      v = __builtin_fmaf(wb0, xb4.x, v);
+      v = __builtin_fmaf(wb1, xb4.y, v);
+      v = __builtin_fmaf(wb2, xb4.z, v);
+      v = __builtin_fmaf(wb3, xb4.w, v);
+      acc_a[m] = u;
+      acc_b[m] = v;
+    }
+  }
+}
+
 template <int M, int LPR, int NT, bool DSC>
 __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
     const float* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
@@ -84,8 +157,6 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
   extern __shared__ float smem[];
   const int XSTR = (KC >> 6) * 68;  // floats per x row in LDS (64 + 4 pad per piece)
   float* xs = smem;                 // [M][KC/64][68]
-  float* sx = smem + M * XSTR;      // [M][KC/32] chunk sums of x
-  const int KC32 = KC >> 5;
   constexpr int S = NT / LPR;
   const int tid = threadIdx.x;
   const int slot = tid / LPR;
@@ -99,9 +170,6 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
   const uint32_t wo = nl * (uint32_t)nsb * (uint32_t)kQ4kBlockBytes;
 
   const uint32_t magic = vreg_const(0x64006400u);
-  const f16x2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  const f16x2 m64 = {(_Float16)-64.0f, (_Float16)-64.0f};
-  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
 
   auto load = [&](Q4kPiece& st, int sb) {
     const uint32_t bo = wo + (uint32_t)sb * kQ4kBlockBytes;
@@ -116,9 +184,9 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
     }
   };
 
-  float acc[M];
+  float acc_a[M], acc_b[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+  for (int m = 0; m < M; ++m) acc_a[m] = acc_b[m] = 0.f;
 
 #pragma unroll 1
   for (int kc = 0; kc < K; kc += KC) {
@@ -156,16 +224,6 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
       }
     }
     __syncthreads();
-    const int nch = kn >> 5;
-    for (int t = tid; t < M * nch; t += NT) {
-      const int m = t / nch, c = t - m * nch;
-      const float* src = xs + m * XSTR + (c >> 1) * 68 + 32 * (c & 1);
-      float s = 0.f;
-#pragma unroll
-      for (int l = 0; l < 32; ++l) s += src[l];
-      sx[m * KC32 + c] = s;
-    }
-    __syncthreads();
 
 #pragma unroll 1
     for (int p = j; p < P; p += LPR) {
@@ -174,73 +232,20 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
       if (more) load(nxt, sb0 + ((p + LPR) >> 2));
 
       float dva, mva, dvb, mvb;
-      if constexpr (DSC) {
-        dva = cur.ea.x; mva = cur.ea.y; dvb = cur.eb.x; mvb = cur.eb.y;
-      } else {
-        uint32_t s2, m2;
-        scale_min_pair(cur.h.y, cur.h.z, cur.h.w, g, s2, m2);
-        const float d = f16_to_f32(cur.h.x & 0xFFFFu);
-        const float dmin = f16_to_f32(cur.h.x >> 16);
-        dva = d * (float)(s2 & 0xFFu);
-        dvb = d * (float)(s2 >> 8);
-        mva = -(dmin * (float)(m2 & 0xFFu));
-        mvb = -(dmin * (float)(m2 >> 8));
-      }
-
-      float pa[M], pb[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) pa[m] = pb[m] = 0.f;
-      const float* xa = xs + p * 68;  // chunk 2g; chunk 2g+1 at +32
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t word = t < 4 ? word_of(cur.q0, t) : word_of(cur.q1, t - 4);
-        const uint32_t w8 = word >> 8;
-        // chunk 2g: low nibbles of bytes (0,2) and (1,3); chunk 2g+1: high nibbles
-        const f16x2 A = bitcast<f16x2>((word & 0x000F000Fu) | magic) + m1024;
-        const f16x2 C = bitcast<f16x2>((w8 & 0x000F000Fu) | magic) + m1024;
-        const f16x2 B =
-            __builtin_elementwise_fma(bitcast<f16x2>((word & 0x00F000F0u) | magic), sixteenth, m64);
-        const f16x2 D =
-            __builtin_elementwise_fma(bitcast<f16x2>((w8 & 0x00F000F0u) | magic), sixteenth, m64);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const float4 xa4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 4 * t);
-          const float4 xb4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 32 + 4 * t);
-          float u = pa[m], v = pb[m];
-          u = __builtin_fmaf((float)A.x, xa4.x, u);
-          u = __builtin_fmaf((float)C.x, xa4.y, u);
-          u = __builtin_fmaf((float)A.y, xa4.z, u);
-          u = __builtin_fmaf((float)C.y, xa4.w, u);
-          v = __builtin_fmaf((float)B.x, xb4.x, v);
-          v = __builtin_fmaf((float)D.x, xb4.y, v);
-          v = __builtin_fmaf((float)B.y, xb4.z, v);
-          v = __builtin_fmaf((float)D.y, xb4.w, v);
-          pa[m] = u;
-          pb[m] = v;
-        }
-      }
-      const int ca = 2 * p;  // chunk index within this K-chunk (= 8*(p/4) + 2g)
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float a = acc[m];
-        a = __builtin_fmaf(dva, pa[m], a);
-        a = __builtin_fmaf(mva, sx[m * KC32 + ca], a);
-        a = __builtin_fmaf(dvb, pb[m], a);
-        a = __builtin_fmaf(mvb, sx[m * KC32 + ca + 1], a);
-        acc[m] = a;
-      }
+      piece_coeffs<DSC>(cur, g, dva, mva, dvb, mvb);
+      piece_mac<M>(cur, xs + p * 68, XSTR, dva, mva, dvb, mvb, magic, acc_a, acc_b);
       if (more) cur = nxt;
     }
   }
 
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const float v = group_sum<LPR>(acc[m]);
+    const float v = group_sum<LPR>(acc_a[m] + acc_b[m]);
     if (j == 0 && n < N) y[m * ldy + n] = v;
   }
 }
 
-// Persistent variant, used whenever x and its chunk sums fit in LDS: one
+// Persistent variant, used whenever x fits in LDS: one
 // resident round of workgroups; each stages x once and splits an equal,
 // contiguous share of rows among its wavefronts.  A wavefront owns one row at
 // a time (LPR = 64) and walks a flat sequence of (row, piece) items with a
@@ -258,8 +263,6 @@ void q4k_gemv_persistent(
   extern __shared__ float smem[];
   const int XSTR = (K >> 6) * 68;  // floats per x row in LDS (64 + 4 pad per piece)
   float* xs = smem;                // [M][K/64][68]
-  float* sx = smem + M * XSTR;     // [M][K/32] chunk sums of x
-  const int K32 = K >> 5;
   const int tid = threadIdx.x;
   const int wv = tid / kWave;
   const int j = tid % kWave;
@@ -280,9 +283,6 @@ void q4k_gemv_persistent(
   const int nitems = nrows * PPI;
 
   const uint32_t magic = vreg_const(0x64006400u);
-  const f16x2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  const f16x2 m64 = {(_Float16)-64.0f, (_Float16)-64.0f};
-  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
 
   auto load = [&](Q4kPiece& st, int row, int it) {
     row = row < N ? row : N - 1;  // a bound only: loaded items never pass the last row
@@ -318,15 +318,12 @@ void q4k_gemv_persistent(
     }
   };
 
-  // Stage x; the chunk sums come out of the same pass when x is 16-byte
-  // aligned (8 consecutive lanes hold one 32-element chunk).  Decoding in
-  // the kernel, a thread issues its weight loads once its x slots are in:
+  // Stage x.  Decoding in the kernel, a thread issues its weight loads once
+  // its x slots are in:
   // behind the weight stream of the whole grid, x would arrive late (measured
   // 0.2-0.5 us per call on the 7B layer shapes).  With the plane, the ring's
   // first loads go out right behind the x loads (measured better there).
   if (x_vec16) {
-    // K is a multiple of 256, so M * K / 4 is a multiple of 64: whole
-    // wavefronts stage together and the 8-lane DPP sum is well defined.
     const int v4 = K >> 2;
     stage_slots<2>(
         tid, NT, M * v4,
@@ -337,10 +334,7 @@ void q4k_gemv_persistent(
         [&](int t, uint4 u) {
           const int m = t / v4, i = t - m * v4;
           const int e = 4 * i;
-          const float4 v = bitcast<float4>(u);
-          *reinterpret_cast<float4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) = v;
-          const float part = group_sum<8>((v.x + v.y) + (v.z + v.w));
-          if ((i & 7) == 0) sx[m * K32 + (i >> 3)] = part;
+          *reinterpret_cast<uint4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) = u;
         },
         [&] {
           if constexpr (DSC) fill_ring();
@@ -357,84 +351,24 @@ void q4k_gemv_persistent(
       xs[m * XSTR + (i >> 6) * 68 + (i & 63)] = x[m * ldx + i];
     }
     __syncthreads();
-    for (int t = tid; t < M * K32; t += NT) {
-      const int m = t / K32, c = t - m * K32;
-      const float* src = xs + m * XSTR + (c >> 1) * 68 + 32 * (c & 1);
-      float sum = 0.f;
-#pragma unroll
-      for (int l = 0; l < 32; ++l) sum += src[l];
-      sx[m * K32 + c] = sum;
-    }
-    __syncthreads();
   }
 
-  float acc[M];
+  float acc_a[M], acc_b[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+  for (int m = 0; m < M; ++m) acc_a[m] = acc_b[m] = 0.f;
 
   auto consume = [&](const Q4kPiece& cur, int row, int it) {
     const int p = j + kWave * it;
     if (p < P) {
       float dva, mva, dvb, mvb;
-      if constexpr (DSC) {
-        dva = cur.ea.x; mva = cur.ea.y; dvb = cur.eb.x; mvb = cur.eb.y;
-      } else {
-        uint32_t s2, m2;
-        scale_min_pair(cur.h.y, cur.h.z, cur.h.w, g, s2, m2);
-        const float d = f16_to_f32(cur.h.x & 0xFFFFu);
-        const float dmin = f16_to_f32(cur.h.x >> 16);
-        dva = d * (float)(s2 & 0xFFu);
-        dvb = d * (float)(s2 >> 8);
-        mva = -(dmin * (float)(m2 & 0xFFu));
-        mvb = -(dmin * (float)(m2 >> 8));
-      }
-      float pa[M], pb[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) pa[m] = pb[m] = 0.f;
-      const float* xa = xs + p * 68;  // chunk 2g; chunk 2g+1 at +32
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t word = t < 4 ? word_of(cur.q0, t) : word_of(cur.q1, t - 4);
-        const uint32_t w8 = word >> 8;
-        const f16x2 A = bitcast<f16x2>((word & 0x000F000Fu) | magic) + m1024;
-        const f16x2 C = bitcast<f16x2>((w8 & 0x000F000Fu) | magic) + m1024;
-        const f16x2 B = __builtin_elementwise_fma(
-            bitcast<f16x2>((word & 0x00F000F0u) | magic), sixteenth, m64);
-        const f16x2 D2 = __builtin_elementwise_fma(
-            bitcast<f16x2>((w8 & 0x00F000F0u) | magic), sixteenth, m64);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const float4 xa4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 4 * t);
-          const float4 xb4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 32 + 4 * t);
-          float u0 = pa[m], v0 = pb[m];
-          u0 = __builtin_fmaf((float)A.x, xa4.x, u0);
-          u0 = __builtin_fmaf((float)C.x, xa4.y, u0);
-          u0 = __builtin_fmaf((float)A.y, xa4.z, u0);
-          u0 = __builtin_fmaf((float)C.y, xa4.w, u0);
-          v0 = __builtin_fmaf((float)B.x, xb4.x, v0);
-          v0 = __builtin_fmaf((float)D2.x, xb4.y, v0);
-          v0 = __builtin_fmaf((float)B.y, xb4.z, v0);
-          v0 = __builtin_fmaf((float)D2.y, xb4.w, v0);
-          pa[m] = u0;
-          pb[m] = v0;
-        }
-      }
-      const int ca = 2 * p;
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float a = acc[m];
-        a = __builtin_fmaf(dva, pa[m], a);
-        a = __builtin_fmaf(mva, sx[m * K32 + ca], a);
-        a = __builtin_fmaf(dvb, pb[m], a);
-        a = __builtin_fmaf(mvb, sx[m * K32 + ca + 1], a);
-        acc[m] = a;
-      }
+      piece_coeffs<DSC>(cur, g, dva, mva, dvb, mvb);
+      piece_mac<M>(cur, xs + p * 68, XSTR, dva, mva, dvb, mvb, magic, acc_a, acc_b);
     }
     if (it == PPI - 1) {  // row finished (uniform across the wavefront)
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const float v = group_sum<kWave>(acc[m]);
-        acc[m] = 0.f;
+        const float v = group_sum<kWave>(acc_a[m] + acc_b[m]);
+        acc_a[m] = acc_b[m] = 0.f;
         if (j == 0) y[m * ldy + row] = v;
       }
     }
@@ -519,7 +453,7 @@ hipError_t launch_persistent(const float* x, int64_t ldx, const uint8_t* w, cons
 }
 
 // Persistent kernel (1024 threads: 16 rows in flight per workgroup, x staged
-// once) whenever x and its chunk sums fit in a workgroup's LDS (up to 160 KB);
+// once) whenever x fits in a workgroup's LDS (up to 160 KB);
 // otherwise the K-chunked tiled kernel (256 threads: it keeps the full
 // register file for its M accumulators per row).
 template <int M>
@@ -528,8 +462,8 @@ hipError_t launch_m(const float* x, int64_t ldx, const uint8_t* w, const float* 
   constexpr int NT = 1024, LPR = 64, NT_TILED = 256;
   const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 4 == 0);
   const float2* dsc2 = reinterpret_cast<const float2*>(dsc);
-  // x (68 floats per 64 elements) plus its chunk sums (2 floats per 64), fp32.
-  const size_t full = (size_t)M * ((K / 64) * 68 + K / 32) * 4;
+  // x as fp32, 68 floats per 64 elements.
+  const size_t full = (size_t)M * (K / 64) * 68 * 4;
   if (full <= (size_t)kLdsMax) {
     // One item per lane in flight over a full grid measured faster than
     // deeper rings on fewer workgroups (4096 x 11008 and 11008 x 4096, M = 1).
@@ -543,9 +477,9 @@ hipError_t launch_m(const float* x, int64_t ldx, const uint8_t* w, const float* 
     constexpr int S = NT_TILED / LPR;
     const int grid = (N + S - 1) / S;
     // KC a multiple of 256 (whole super-blocks) within the LDS budget.
-    int KC = (kLdsBudget / (4 * 70 * M)) * 64 & ~255;
+    int KC = (kLdsBudget / (4 * 68 * M)) * 64 & ~255;
     if (KC > K) KC = K;
-    const size_t shmem = (size_t)M * ((KC / 64) * 68 + KC / 32) * 4;
+    const size_t shmem = (size_t)M * (KC / 64) * 68 * 4;
     if (dsc)
       hipLaunchKernelGGL((q4k_gemv_kernel<M, LPR, NT_TILED, true>), dim3(grid), dim3(NT_TILED),
                          shmem, stream, x, ldx, w, dsc2, y, ldy, N, K, KC, x_vec16);
@@ -566,7 +500,7 @@ hipError_t launch_q4k_gemv(const float* x, int64_t ldx, const uint8_t* w, const 
   // weights, which beats restaging x for every 4 rows in the tiled kernel.
   // Rows too long for LDS go to the K-chunked tiled kernel, at most 4 rows of
   // x at a time (its per-row accumulators would spill beyond that).
-  const size_t per_row = ((size_t)(K / 64) * 68 + K / 32) * 4;
+  const size_t per_row = (size_t)(K / 64) * 68 * 4;
   const int mfit = (size_t)kLdsMax >= per_row ? (int)((size_t)kLdsMax / per_row) : (M < 4 ? M : 4);
   if (M > mfit) {
     for (int m0 = 0; m0 < M; m0 += mfit) {
