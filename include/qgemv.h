@@ -78,7 +78,10 @@ typedef enum qg_dtype {
  *     w[n,k] = float(s) * (q - zp)       (exact in binary32)
  *     y[m,n] = sum_k x[m,k] * w[n,k]
  *
- * x           : fp16 bits, [M][ldx], 2-byte aligned.
+ * x           : [M][ldx] of x_type, 2-byte aligned.
+ * x_type      : QG_F16 (IEEE binary16).  QG_BF16 activations are not
+ *               provided and return QG_ERR_UNSUPPORTED (nothing enqueued);
+ *               any other value is QG_ERR_UNSUPPORTED as well.
  * w           : [N][K/2] bytes, 16-byte aligned.
  * scales      : fp16 bits, [N][K/block_size], 2-byte aligned.
  * zero_points : [N][ZR] bytes or NULL (symmetric, zero point 8).  In a row
@@ -88,8 +91,8 @@ typedef enum qg_dtype {
  * block_size  : 32, 64, 128 or 256 (QG_ERR_UNSUPPORTED otherwise); K must be
  *               a positive multiple of it (QG_ERR_BAD_SHAPE otherwise).
  */
-qg_status qgemv_int4_blockwise(const uint16_t *x, int64_t ldx, const uint8_t *w,
-                               const uint16_t *scales,
+qg_status qgemv_int4_blockwise(const void *x, int64_t ldx, int32_t x_type,
+                               const uint8_t *w, const uint16_t *scales,
                                const uint8_t *zero_points, void *y, int64_t ldy,
                                int32_t y_type, int64_t M, int64_t N, int64_t K,
                                int32_t block_size, void *stream);
@@ -241,9 +244,11 @@ const char *qg_last_error(void);
 
 /*
  * Liveness and explain trace (for callers that dispatch on top of this
- * library).  A fast path that degrades correctly must carry a visible label,
- * because parity cannot see which path ran ("62 . r59 -- q4_K W_dsc plane +
- * riders", section 3.1, "Failure must be loud"; section 4, liveness).
+ * library).  Which kernel path produced a result cannot be told from the
+ * result, so every launch is counted and described by name; a caller that
+ * falls back from a fast path can then report it ("62 . r59 -- q4_K W_dsc
+ * plane + riders", section 3.1, on failures that must not go unnoticed;
+ * section 4, liveness).
  *
  * qg_last_launch   : the kernels enqueued by the calling thread's last library
  *                    call, as "path M=.. grid=.. block=.. lds=.." entries

@@ -6,7 +6,9 @@ package binding.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import functools
+import os
 import sys
 
 import numpy as np
@@ -81,3 +83,34 @@ def q4k_ref(N, K, seed, M=datagen.X_ROWS, cols=None):
 @functools.lru_cache(maxsize=None)
 def bf16_case(N, K, seed):
     return datagen.bf16_problem(N, K, seed)
+
+
+def oracle_threads() -> int:
+    """Host threads for the oracle: the cores this process may use, at most
+    16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_all_columns(fn, N, *args, **kw):
+    """(y_ref, S) of every column of an oracle GEMV ``fn(*args, cols=...)``,
+    computed over column ranges on host threads (the oracle's C calls release
+    the GIL; columns are independent, so the result is the same as one call)."""
+    t = oracle_threads()
+    bounds = [(i * N) // t for i in range(t + 1)]
+    ranges = [np.arange(bounds[i], bounds[i + 1]) for i in range(t) if bounds[i + 1] > bounds[i]]
+    with concurrent.futures.ThreadPoolExecutor(len(ranges)) as ex:
+        parts = list(ex.map(lambda c: fn(*args, cols=c, **kw), ranges))
+    return (np.concatenate([p[0] for p in parts], axis=1),
+            np.concatenate([p[1] for p in parts], axis=1))
+
+
+@functools.lru_cache(maxsize=None)
+def int4_ref_all(N, K, bs, asym, seed):
+    """All X_ROWS rows of x against every column, on host threads."""
+    p = int4_case(N, K, bs, asym, seed)
+    return oracle_all_columns(oracle.int4_gemv, N, p.x, p.w, p.scales, p.zp, datagen.X_ROWS, N,
+                              K, bs)

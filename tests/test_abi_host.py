@@ -80,8 +80,8 @@ D = 0x7F0300000000
 E = 0x7F0400000000
 
 
-def _int4(L, x=A, ldx=64, w=B, s=C, zp=D, y=E, ldy=16, yt=0, M=1, N=16, K=64, bs=32):
-    return L.qgemv_int4_blockwise(x, ldx, w, s, zp, y, ldy, yt, M, N, K, bs, None)
+def _int4(L, x=A, ldx=64, w=B, s=C, zp=D, y=E, ldy=16, yt=0, M=1, N=16, K=64, bs=32, xt=0):
+    return L.qgemv_int4_blockwise(x, ldx, xt, w, s, zp, y, ldy, yt, M, N, K, bs, None)
 
 
 def test_int4_validation():
@@ -98,6 +98,10 @@ def test_int4_validation():
     assert _int4(L, bs=16) == QG_ERR_UNSUPPORTED
     assert _int4(L, bs=48) == QG_ERR_UNSUPPORTED
     assert _int4(L, yt=7) == QG_ERR_UNSUPPORTED
+    # activations: fp16 only; bf16 (and anything else) is refused, not converted
+    assert _int4(L, xt=1) == QG_ERR_UNSUPPORTED
+    assert "x_type" in L.qg_last_error().decode()
+    assert _int4(L, xt=2) == QG_ERR_UNSUPPORTED
     assert _int4(L, ldx=32) == QG_ERR_BAD_SHAPE
     assert _int4(L, ldy=8) == QG_ERR_BAD_SHAPE
     assert _int4(L, w=B + 8) == QG_ERR_MISALIGNED
@@ -261,3 +265,52 @@ def test_liveness_exports_on_the_host():
     counts = q.path_launches()
     assert set(counts) == set(names) and all(v >= 0 for v in counts.values())
     assert isinstance(q.last_launch(), str)
+
+
+def test_binding_refuses_mismatched_shapes_before_the_call():
+    """Sizes come from x and w; every other tensor must match them, or the
+    library would read or write past its end.  These raise before any call
+    (host tensors, no GPU needed)."""
+    f16, u8 = torch.float16, torch.uint8
+    x = torch.zeros(1, 64, dtype=f16)
+    w = torch.zeros(4, 32, dtype=u8)
+    s = torch.zeros(4, 2, dtype=f16)
+    zp = torch.zeros(4, 1, dtype=u8)
+    y = torch.zeros(1, 4, dtype=f16)
+    bad = {
+        "y": dict(y=torch.zeros(4, 4, dtype=f16)),          # x [1,K] with y [4,N]
+        "w": dict(w=torch.zeros(4, 16, dtype=u8)),
+        "scales": dict(s=torch.zeros(4, 1, dtype=f16)),
+        "zero_points": dict(zp=torch.zeros(4, 2, dtype=u8)),
+    }
+    for name, kw in bad.items():
+        args = dict(x=x, w=w, s=s, zp=zp, y=y)
+        args.update(kw)
+        with pytest.raises(ValueError, match=name):
+            q.qgemv_int4_blockwise(args["x"], args["w"], args["s"], args["zp"], args["y"], 32,
+                                   stream=0)
+    with pytest.raises(ValueError, match="contiguous"):
+        q.qgemv_int4_blockwise(x, torch.zeros(32, 4, dtype=u8).t(), s, zp, y, 32, stream=0)
+    # q4_K: y, w and the plane
+    xq, wq = torch.zeros(2, 256), torch.zeros(4, 144, dtype=u8)
+    with pytest.raises(ValueError, match="y"):
+        q.qgemv_q4k(xq, wq, torch.zeros(1, 4), stream=0)
+    with pytest.raises(ValueError, match="w"):
+        q.qgemv_q4k(xq, torch.zeros(4, 288, dtype=u8), torch.zeros(2, 4), stream=0)
+    with pytest.raises(ValueError, match="dsc"):
+        q.qgemv_q4k_dsc(xq, wq, torch.zeros(8 * 4 - 1, 2), torch.zeros(2, 4), stream=0)
+    with pytest.raises(ValueError, match="dsc_out"):
+        q.q4k_build_dsc_plane(wq, torch.zeros(16, 2), 4, 256, stream=0)
+    # bf16: w rows of another length
+    with pytest.raises(ValueError, match="w"):
+        q.gemv_bf16(torch.zeros(1, 8, dtype=torch.bfloat16), torch.zeros(4, 16, dtype=torch.bfloat16),
+                    torch.zeros(1, 4, dtype=torch.bfloat16), stream=0)
+    # prefill: codes, scales, y
+    xt = torch.zeros(3, 256)
+    with pytest.raises(ValueError, match="qa"):
+        q.q8_quantize_rows(xt, torch.zeros(2, 256, dtype=torch.int8), torch.zeros(3, 8, 2), stream=0)
+    with pytest.raises(ValueError, match="sda"):
+        q.q8_quantize_rows(xt, torch.zeros(3, 256, dtype=torch.int8), torch.zeros(3, 4, 2), stream=0)
+    with pytest.raises(ValueError, match="y"):
+        q.qgemm_q4k_mmq(xt, wq, torch.zeros(32, 2), torch.zeros(3, 5), torch.zeros(4096, dtype=u8),
+                        stream=0)

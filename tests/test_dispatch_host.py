@@ -167,3 +167,38 @@ def test_prefill_workspace_grows_per_stream(fake_abi):
     assert [c[2] for c in fake_abi if c[0] == "mmq"] == [400, 400, 640, 160]
     dispatch._workspaces.clear()
     dispatch.unregister_q4k_plane(w)
+
+
+def test_plane_entry_is_keyed_on_shape_and_dropped_with_the_weight(fake_abi):
+    import gc
+
+    w = _q4k_weights(16, 512)
+    assert dispatch.register_q4k_plane(w)
+    # another view of the same bytes with another shape finds no plane
+    w2 = w.view(32, 144)
+    assert dispatch.q4k_plane_of(w2) is None
+    _, label = dispatch.q4k_linear(torch.zeros((1, 256)), w2)
+    assert label == dispatch.LABEL_OFF
+    key = (w.data_ptr(), 16, 512)
+    del w2
+    del w
+    gc.collect()
+    # the weight is gone: a tensor that later reuses its address must not meet
+    # the old plane
+    assert key not in dispatch._planes and key not in dispatch._failed
+
+
+def test_failed_registration_is_dropped_with_the_weight(fake_abi, monkeypatch):
+    import gc
+
+    def failing_build(w, dsc, N, K, stream=None):
+        raise qgemv.QgemvError("q4k_build_dsc_plane", 6, "QG_ERR_HIP", "simulated")
+
+    monkeypatch.setattr(qgemv, "q4k_build_dsc_plane", failing_build)
+    w = _q4k_weights(8, 256)
+    key = (w.data_ptr(), 8, 256)
+    assert not dispatch.register_q4k_plane(w)
+    assert key in dispatch._failed
+    del w
+    gc.collect()
+    assert key not in dispatch._failed

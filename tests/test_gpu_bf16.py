@@ -25,14 +25,17 @@ def _ref(p, M, cols=None, ldw=None, wbuf=None, xbuf=None, ldx=None):
 
 @pytest.mark.parametrize("N,K,seed", [(1536, 1536, 301), (256, 1536, 302), (1536, 6912, 303),
                                       (6912, 1536, 304)])
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("M", list(range(1, 9)))
 def test_decode_shapes(N, K, seed, M):
     p = bf16_case(N, K, seed)
     say(f"bf16 N={N} K={K} M={M}")
     y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     q.gemv_bf16(bf16_dev(p.x[:M]), bf16_dev(p.w), y)
+    launch = q.last_launch()
+    # aligned x and W: the v_dot2 kernel at M = 1, the matrix cores from M = 2
+    assert ("bf16_aligned" if M == 1 else "bf16_mfma_") in launch, launch
     yr, S = _ref(p, M)
-    assert_accept(y_host(y), yr, S, "bf16", f"bf16 {N}x{K} M={M}")
+    assert_accept(y_host(y), yr, S, "bf16", f"bf16 {N}x{K} M={M} ({launch})")
 
 
 @pytest.mark.parametrize("N", [256, 1536])
@@ -112,6 +115,67 @@ def test_one_hot_probe_matrix_core_path_is_bit_exact(K):
         assert np.array_equal(got, want), kk
         nz = want != 0
         assert np.array_equal(got.view(np.uint32)[nz], want.view(np.uint32)[nz]), kk
+
+
+def _one_hot_expected(p, ks, xbuf_rows=None):
+    """The oracle's y for one-hot rows of x (row i one-hot at ks[i]), as
+    float32: each is a bf16 weight, exactly representable."""
+    K = p.K
+    x = np.zeros((len(ks), K), dtype=np.uint16)
+    for i, k in enumerate(ks):
+        x[i, k] = 0x3F80  # bf16 1.0
+    yr, _ = oracle.bf16_gemv(x, p.w, len(ks), p.N, K, K, K)
+    assert np.array_equal(yr.astype(np.float32).astype(np.float64), yr)
+    return x, yr.astype(np.float32)
+
+
+@pytest.mark.parametrize("N,K,path", [(300, 1024, "bf16_aligned"), (64, 1536, "bf16_aligned"),
+                                      (300, 1534, "bf16_general"), (48, 100, "bf16_general")])
+def test_one_hot_probe_single_row_is_bit_exact(N, K, path):
+    """M = 1, fp32 out: y[n] must equal w[n, k] bitwise, the expected value
+    coming from the oracle (x = e_k).  K = 1024 / 1536 with aligned rows take
+    the v_dot2 kernel; K = 1534 / 100 (rows not 16-byte multiples) the
+    anchored general kernel."""
+    p = bf16_case(N, K, 370 + K)
+    wd = bf16_dev(p.w)
+    ks = sorted(set(list(range(0, K, max(1, K // 97))) + [1, 7, 8, K - 2, K - 1]))
+    x, want = _one_hot_expected(p, ks)
+    xd = bf16_dev(x)
+    say(f"bf16 one-hot M=1 N={N} K={K} ({path}): {len(ks)} positions")
+    got = np.empty((len(ks), N), dtype=np.float32)
+    for i in range(len(ks)):
+        y = torch.empty((1, N), dtype=torch.float32, device=DEV)
+        q.gemv_bf16(xd[i:i + 1], wd, y)
+        assert path in q.last_launch(), q.last_launch()
+        got[i] = y.cpu().numpy()[0]
+    assert np.array_equal(got, want)
+    nz = want != 0
+    assert np.array_equal(got.view(np.uint32)[nz], want.view(np.uint32)[nz])
+
+
+@pytest.mark.parametrize("off", [1, 3])
+def test_one_hot_probe_general_path_offsets_is_bit_exact(off):
+    """The anchored general kernel with W and x at odd 2-byte offsets (every
+    row its own alignment), M = 3: row r of x one-hot at k_r."""
+    N, K, M = 200, 1000, 3
+    p = bf16_case(N, K, 380 + off)
+    wbuf = np.zeros(off + N * K, dtype=np.uint16)
+    wbuf[off:] = p.w.ravel()
+    wd = bf16_dev(wbuf)[off:].view(N, K)
+    ks = list(range(0, K, 11)) + [K - 1]
+    x_all, want_all = _one_hot_expected(p, ks)
+    say(f"bf16 one-hot general path offset={off}: {len(ks)} positions")
+    for i0 in range(0, len(ks), M):
+        rows = x_all[i0:i0 + M]
+        MM = rows.shape[0]
+        xbuf = np.zeros(off + MM * K, dtype=np.uint16)
+        xbuf[off:] = rows.ravel()
+        xd = bf16_dev(xbuf)[off:].view(MM, K)
+        y = torch.empty((MM, N), dtype=torch.float32, device=DEV)
+        q.gemv_bf16(xd, wd, y)
+        assert "bf16_general" in q.last_launch(), q.last_launch()
+        got = y.cpu().numpy()
+        assert np.array_equal(got, want_all[i0:i0 + MM]), ks[i0:i0 + MM]
 
 
 @pytest.mark.parametrize("M", [2, 5])

@@ -140,13 +140,17 @@ uint64_t qg_path_launches(int32_t path) {
              : 0;
 }
 
-qg_status qgemv_int4_blockwise(const uint16_t* x, int64_t ldx, const uint8_t* w,
+qg_status qgemv_int4_blockwise(const void* xv, int64_t ldx, int32_t x_type, const uint8_t* w,
                                const uint16_t* scales, const uint8_t* zero_points, void* y,
                                int64_t ldy, int32_t y_type, int64_t M, int64_t N, int64_t K,
                                int32_t block_size, void* stream) {
   begin_call();
   static const char fn[] = "qgemv_int4_blockwise";
+  const uint16_t* x = static_cast<const uint16_t*>(xv);
   if (!x || !w || !scales || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w, scales and y are required", fn);
+  if (x_type != QG_F16)
+    return fail(QG_ERR_UNSUPPORTED, "%s: x_type %d (only QG_F16 activations are provided)", fn,
+                x_type);
   if (qg_status s = check_mnk(fn, M, N, K)) return s;
   if (block_size != 32 && block_size != 64 && block_size != 128 && block_size != 256)
     return fail(QG_ERR_UNSUPPORTED, "%s: block_size %d not in {32, 64, 128, 256}", fn, block_size);

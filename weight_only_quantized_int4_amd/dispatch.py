@@ -3,11 +3,12 @@ liveness labels, and row groups for any number of rows of x.
 
 q4_K plane ("62 . r59 -- q4_K W_dsc plane + riders", section 3.1): the plane of
 a weight is built once at load time and kept in a map keyed by the weight's
-device pointer.  A call takes the plane when one is registered.  When a
-registration failed, the call degrades to in-kernel decode, with a warning
-once per process and a visible label: "a fast path that degrades correctly
-must carry a visible label", because parity cannot see the path.  Labels
-(counted by ``liveness()``):
+device pointer and shape (N, K); the entry is dropped when the weight tensor
+is freed, so a later tensor at a reused address never meets a stale plane.
+A call takes the plane when one is registered.  When a registration failed,
+the call degrades to in-kernel decode, with a warning once per process and a
+label that says so: which path ran cannot be told from the result, so a
+silent degradation would go unnoticed.  Labels (counted by ``liveness()``):
 
     dsc-plane             the plane was used
     in-kernel(dsc=off)    no plane registered for this weight, or the plane
@@ -38,6 +39,7 @@ from __future__ import annotations
 import os
 import threading
 import warnings
+import weakref
 from typing import Optional, Tuple
 
 import torch
@@ -51,8 +53,9 @@ LABEL_FALLBACK = "in-kernel(fallback!)"
 LABEL_MMQ = "mmq(q8 activations)"
 
 _lock = threading.Lock()
-_planes = {}   # weight device pointer -> plane tensor
-_failed = {}   # weight device pointer -> reason the registration failed
+_planes = {}   # (weight device pointer, N, K) -> plane tensor
+_failed = {}   # (weight device pointer, N, K) -> reason the registration failed
+_finalizers = {}  # (weight device pointer, N, K) -> weakref.finalize on the weight tensor
 _warned = False
 _liveness = {LABEL_PLANE: 0, LABEL_OFF: 0, LABEL_FALLBACK: 0, LABEL_MMQ: 0}
 _workspaces = {}  # (device index, stream handle) -> uint8 workspace of the prefill product
@@ -94,14 +97,39 @@ def q4k_shape(w: torch.Tensor) -> Tuple[int, int]:
     return w.shape[0], w.shape[1] // 144 * 256
 
 
+def _key(w: torch.Tensor):
+    N, K = q4k_shape(w)
+    return (w.data_ptr(), N, K)
+
+
+def _forget(key) -> None:
+    with _lock:
+        _planes.pop(key, None)
+        _failed.pop(key, None)
+        _finalizers.pop(key, None)
+
+
+def _track(key, w: torch.Tensor) -> None:
+    """Drop the registry entry of ``key`` when the tensor ``w`` is freed."""
+    with _lock:
+        if key in _finalizers and _finalizers[key].alive:
+            return
+        _finalizers[key] = weakref.finalize(w, _forget, key)
+
+
 def register_q4k_plane(w: torch.Tensor, stream=None) -> bool:
     """Build the W_dsc plane of raw q4_K weights ``w`` and register it under
-    w's device pointer.  Returns False, and remembers why, when the plane
-    cannot be allocated or built; calls on ``w`` then fall back to in-kernel
-    decode with the fallback label."""
-    key = w.data_ptr()
+    w's device pointer and shape.  Returns False, and remembers why, when the
+    plane cannot be allocated or built; calls on ``w`` then fall back to
+    in-kernel decode with the fallback label.  The entry lives as long as the
+    tensor ``w``."""
     try:
         N, K = q4k_shape(w)
+    except ValueError:
+        return False  # not a q4_K weight: no entry, calls on it are refused too
+    key = (w.data_ptr(), N, K)
+    _track(key, w)
+    try:
         nbytes = _q.q4k_dsc_plane_bytes(N, K)
         if nbytes == 0 and N > 0:
             raise ValueError(f"no plane for N={N}, K={K}")
@@ -119,14 +147,17 @@ def register_q4k_plane(w: torch.Tensor, stream=None) -> bool:
 
 
 def unregister_q4k_plane(w: torch.Tensor) -> None:
+    key = _key(w)
     with _lock:
-        _planes.pop(w.data_ptr(), None)
-        _failed.pop(w.data_ptr(), None)
+        fin = _finalizers.get(key)
+    if fin is not None:
+        fin.detach()
+    _forget(key)
 
 
 def q4k_plane_of(w: torch.Tensor) -> Optional[torch.Tensor]:
     with _lock:
-        return _planes.get(w.data_ptr())
+        return _planes.get(_key(w))
 
 
 def _row_groups(M: int):
@@ -151,7 +182,7 @@ def q4k_linear(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = Non
     M = x.shape[0]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    key = w.data_ptr()
+    key = (w.data_ptr(), N, K)
     with _lock:
         dsc = _planes.get(key)
         failure = _failed.get(key)

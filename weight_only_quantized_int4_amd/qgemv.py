@@ -1,9 +1,12 @@
 """ctypes binding of libqgemv.so -- argument marshalling only.
 
-Every function takes torch tensors and checks only what the C library cannot
-see through a raw pointer: each tensor's dtype, and that it lives in GPU
-memory (on a machine with a GPU, a host tensor's address would otherwise reach
-a kernel).  It turns shapes into sizes and strides into leading dimensions,
+Every function takes torch tensors and checks what the C library cannot see
+through a raw pointer: each tensor's dtype, that it lives in GPU memory (on a
+machine with a GPU, a host tensor's address would otherwise reach a kernel),
+and that every tensor's shape and layout agree with the sizes taken from x and
+w (a y, scale, zero-point, plane or workspace tensor shorter than the problem
+would otherwise be read or written past its end).  It turns shapes into sizes
+and strides into leading dimensions,
 passes ``data_ptr()`` and the current HIP stream, and raises ``QgemvError``
 with the library's own message on a non-OK status.  All compute happens in the HIP kernels; if the library is missing the
 import of a function fails loudly -- there is no CPU fallback.
@@ -21,6 +24,7 @@ _LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 
 QG_F16, QG_BF16, QG_F32 = 0, 1, 2
 _OUT_TYPES = {torch.float16: QG_F16, torch.bfloat16: QG_BF16, torch.float32: QG_F32}
+_X_TYPES = {torch.float16: QG_F16, torch.bfloat16: QG_BF16}
 
 
 class QgemvError(RuntimeError):
@@ -51,7 +55,7 @@ def load_library() -> ctypes.CDLL:
     L = ctypes.CDLL(_LIB_PATH)
     P, I64, I32, St = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
     sigs = {
-        "qgemv_int4_blockwise": (St, [P, I64, P, P, P, P, I64, I32, I64, I64, I64, I32, P]),
+        "qgemv_int4_blockwise": (St, [P, I64, I32, P, P, P, P, I64, I32, I64, I64, I64, I32, P]),
         "qgemv_q4k": (St, [P, I64, P, P, I64, I64, I64, I64, P]),
         "qgemv_q4k_dsc": (St, [P, I64, P, P, P, I64, I64, I64, I64, P]),
         "gemv_bf16": (St, [P, I64, P, I64, P, I64, I32, I64, I64, I64, P]),
@@ -108,6 +112,31 @@ def _arg(t: Optional[torch.Tensor], name: str, dtypes) -> None:
             raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
 
 
+def _dims(t: torch.Tensor, name: str, shape) -> None:
+    """Refuse a tensor whose shape is not ``shape``."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _dense(t: Optional[torch.Tensor], name: str, shape) -> None:
+    """Refuse a tensor that is not a dense row-major array of ``shape`` (the
+    library reads it as one without a stride)."""
+    if t is None:
+        return
+    _dims(t, name, shape)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (dense row-major)")
+
+
+def _xy(x: torch.Tensor, y: torch.Tensor, N: int):
+    """(M, K) of x [M, K], checking y [M, N]."""
+    if x.dim() != 2:
+        raise ValueError(f"x: expected a 2-D tensor [M, K], got shape {tuple(x.shape)}")
+    M, K = x.shape
+    _dims(y, "y", (M, N))
+    return M, K
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -124,25 +153,41 @@ def _ld(t: torch.Tensor) -> int:
 def qgemv_int4_blockwise(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
                          zero_points: Optional[torch.Tensor], y: torch.Tensor,
                          block_size: int, stream=None) -> torch.Tensor:
-    """y[M,N] = x[M,K] . dequant(w)^T.  x fp16 [M,K]; w uint8 [N,K/2]; scales
-    fp16 [N,K/bs]; zero_points uint8 [N,ceil(K/bs/2)] or None; y fp16/bf16/fp32 [M,N]."""
-    for t, n, d in ((x, "x", _F16), (w, "w", _U8), (scales, "scales", _F16),
+    """y[M,N] = x[M,K] . dequant(w)^T.  x fp16 [M,K] (the library refuses bf16
+    activations with QG_ERR_UNSUPPORTED); w uint8 [N,K/2]; scales fp16
+    [N,K/bs]; zero_points uint8 [N,ceil(K/bs/2)] or None; y fp16/bf16/fp32 [M,N]."""
+    for t, n, d in ((x, "x", tuple(_X_TYPES)), (w, "w", _U8), (scales, "scales", _F16),
                     (zero_points, "zero_points", _U8), (y, "y", _OUT)):
         _arg(t, n, d)
-    M, K = x.shape
+    if w.dim() != 2:
+        raise ValueError(f"w: expected a 2-D tensor [N, K/2], got shape {tuple(w.shape)}")
     N = w.shape[0]
+    M, K = _xy(x, y, N)
+    _dense(w, "w", (N, K // 2))
+    if block_size > 0 and K % block_size == 0:  # otherwise the library rejects the call
+        nb = K // block_size
+        _dense(scales, "scales", (N, nb))
+        _dense(zero_points, "zero_points", (N, (nb + 1) // 2))
     _check("qgemv_int4_blockwise", load_library().qgemv_int4_blockwise(
-        _ptr(x), _ld(x), _ptr(w), _ptr(scales), _ptr(zero_points), _ptr(y), _ld(y),
+        _ptr(x), _ld(x), _X_TYPES[x.dtype], _ptr(w), _ptr(scales), _ptr(zero_points), _ptr(y), _ld(y),
         _OUT_TYPES[y.dtype], M, N, K, block_size, _stream(stream)))
     return y
+
+
+def _q4k_rows(w: torch.Tensor) -> int:
+    if w.dim() != 2:
+        raise ValueError(f"w: expected a 2-D uint8 tensor [N, K/256*144], got shape {tuple(w.shape)}")
+    return w.shape[0]
 
 
 def qgemv_q4k(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
     """q4_K GEMV.  x fp32 [M,K]; w uint8 [N, K/256*144]; y fp32 [M,N]."""
     for t, n, d in ((x, "x", _F32), (w, "w", _U8), (y, "y", _F32)):
         _arg(t, n, d)
-    M, K = x.shape
-    N = w.shape[0]
+    N = _q4k_rows(w)
+    M, K = _xy(x, y, N)
+    if K % 256 == 0:  # otherwise the library rejects the call
+        _dense(w, "w", (N, K // 256 * 144))
     _check("qgemv_q4k", load_library().qgemv_q4k(
         _ptr(x), _ld(x), _ptr(w), _ptr(y), _ld(y), M, N, K, _stream(stream)))
     return y
@@ -153,8 +198,11 @@ def qgemv_q4k_dsc(x: torch.Tensor, w: torch.Tensor, dsc: Optional[torch.Tensor],
     """q4_K GEMV with (dv, mv) read from the W_dsc plane (fp32 [(K/32)*N, 2])."""
     for t, n, d in ((x, "x", _F32), (w, "w", _U8), (dsc, "dsc", _F32), (y, "y", _F32)):
         _arg(t, n, d)
-    M, K = x.shape
-    N = w.shape[0]
+    N = _q4k_rows(w)
+    M, K = _xy(x, y, N)
+    if K % 256 == 0:  # otherwise the library rejects the call
+        _dense(w, "w", (N, K // 256 * 144))
+        _dense(dsc, "dsc", (K // 32 * N, 2))
     _check("qgemv_q4k_dsc", load_library().qgemv_q4k_dsc(
         _ptr(x), _ld(x), _ptr(w), _ptr(dsc), _ptr(y), _ld(y), M, N, K, _stream(stream)))
     return y
@@ -164,8 +212,11 @@ def gemv_bf16(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=None) ->
     """y[M,N] = x[M,K] . w[N,K]^T in bf16 (any K, any 2-byte offset)."""
     for t, n, d in ((x, "x", _BF16), (w, "w", _BF16), (y, "y", _OUT)):
         _arg(t, n, d)
-    M, K = x.shape
+    if w.dim() != 2:
+        raise ValueError(f"w: expected a 2-D tensor [N, K], got shape {tuple(w.shape)}")
     N = w.shape[0]
+    M, K = _xy(x, y, N)
+    _dims(w, "w", (N, K))
     _check("gemv_bf16", load_library().gemv_bf16(
         _ptr(x), _ld(x), _ptr(w), _ld(w), _ptr(y), _ld(y), _OUT_TYPES[y.dtype], M, N, K,
         _stream(stream)))
@@ -181,6 +232,9 @@ def q4k_build_dsc_plane(w: torch.Tensor, dsc_out: torch.Tensor, N: int, K: int,
     """Load-time repack of raw q4_K weights into the chunk-major W_dsc plane."""
     _arg(w, "w", _U8)
     _arg(dsc_out, "dsc_out", _F32)
+    if N >= 0 and K >= 256 and K % 256 == 0:  # otherwise the library rejects the call
+        _dense(w, "w", (N, K // 256 * 144))
+        _dense(dsc_out, "dsc_out", (K // 32 * N, 2))
     _check("q4k_build_dsc_plane", load_library().q4k_build_dsc_plane(
         _ptr(w), _ptr(dsc_out), N, K, _stream(stream)))
     return dsc_out
@@ -194,7 +248,12 @@ def q8_quantize_rows(x: torch.Tensor, qa: torch.Tensor, sda: torch.Tensor, strea
     """8-bit activation prepass.  x fp32 [T,K]; qa int8 [T,K]; sda fp32 [T,K/32,2]."""
     for t, n, d in ((x, "x", _F32), (qa, "qa", _I8), (sda, "sda", _F32)):
         _arg(t, n, d)
+    if x.dim() != 2:
+        raise ValueError(f"x: expected a 2-D tensor [T, K], got shape {tuple(x.shape)}")
     T, K = x.shape
+    _dense(qa, "qa", (T, K))
+    if K % 32 == 0:  # otherwise the library rejects the call
+        _dense(sda, "sda", (T, K // 32, 2))
     _check("q8_quantize_rows", load_library().q8_quantize_rows(
         _ptr(x), _ld(x), _ptr(qa), _ptr(sda), T, K, _stream(stream)))
     return qa, sda
@@ -207,8 +266,13 @@ def qgemm_q4k_mmq(x: torch.Tensor, w: torch.Tensor, dsc: Optional[torch.Tensor],
     for t, n, d in ((x, "x", _F32), (w, "w", _U8), (dsc, "dsc", _F32), (y, "y", _F32),
                     (workspace, "workspace", None)):
         _arg(t, n, d)
-    T, K = x.shape
-    N = w.shape[0]
+    N = _q4k_rows(w)
+    T, K = _xy(x, y, N)
+    if K % 256 == 0:  # otherwise the library rejects the call
+        _dense(w, "w", (N, K // 256 * 144))
+        _dense(dsc, "dsc", (K // 32 * N, 2))
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     _check("qgemm_q4k_mmq", load_library().qgemm_q4k_mmq(
         _ptr(x), _ld(x), _ptr(w), _ptr(dsc), _ptr(y), _ld(y), T, N, K, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
