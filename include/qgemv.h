@@ -234,6 +234,29 @@ qg_status qgemm_q4k_mmq(const float *x, int64_t ldx, const uint8_t *w,
                         int64_t N, int64_t K, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/*
+ * qgemm_q4k_mmq_noalloc -- qgemm_q4k_mmq for callers that cannot allocate
+ * device memory (code recorded under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same two kernels and the same result,
+ * bit for bit, with the workspace taken from a static device array of the
+ * library instead of a caller-owned buffer.  It calls no allocating routine.
+ *
+ * The array holds QG_MMQ_NOALLOC_SCRATCH_BYTES bytes; every GPU the library
+ * runs on keeps its own copy from the library's load until the process ends.
+ * Problems whose q4k_mmq_workspace_bytes(T, K) exceeds it return
+ * QG_ERR_UNSUPPORTED with nothing enqueued (use qgemm_q4k_mmq).  The prepass
+ * overwrites every workspace byte the product reads, so nothing has to start
+ * at zero, but all calls on one GPU share the array: calls that overlap on
+ * one GPU (different streams, or host threads) race and must be serialised
+ * by the caller.
+ * Arguments as in qgemm_q4k_mmq, without the workspace; y must not overlap
+ * x, w or dsc.
+ */
+#define QG_MMQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+qg_status qgemm_q4k_mmq_noalloc(const float *x, int64_t ldx, const uint8_t *w,
+                                const float *dsc, float *y, int64_t ldy,
+                                int64_t T, int64_t N, int64_t K, void *stream);
+
 /* Static English name of a status code ("QG_OK", ...). */
 const char *qg_status_string(qg_status s);
 

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
                             "q4k_dsc_plane_bytes", "q4k_build_dsc_plane", "qg_status_string",
                             "qg_last_error", "qg_last_launch", "qg_path_count", "qg_path_name",
                             "qg_path_launches", "q4k_mmq_workspace_bytes", "q8_quantize_rows",
-                            "qgemm_q4k_mmq"])
+                            "qgemm_q4k_mmq", "qgemm_q4k_mmq_noalloc"])
 
 
 def test_library_exports_exactly_the_header():
@@ -314,3 +314,25 @@ def test_binding_refuses_mismatched_shapes_before_the_call():
     with pytest.raises(ValueError, match="y"):
         q.qgemm_q4k_mmq(xt, wq, torch.zeros(32, 2), torch.zeros(3, 5), torch.zeros(4096, dtype=u8),
                         stream=0)
+
+
+def test_noalloc_prefill_validation_on_the_host():
+    """The allocation-free prefill entry point refuses, before touching the
+    GPU, problems whose workspace exceeds its static array, and shares the
+    other checks of qgemm_q4k_mmq."""
+    L = q.load_library()
+    text = open(HEADER).read()
+    m = re.search(r"#define QG_MMQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == q.MMQ_NOALLOC_SCRATCH_BYTES
+
+    def call(x=A, ldx=4096, w=B, dsc=C, y=E, ldy=16, T=4, N=16, K=4096):
+        return L.qgemm_q4k_mmq_noalloc(x, ldx, w, dsc, y, ldy, T, N, K, None)
+
+    # 8192 rows of 4096: 40 MiB of codes and scales > the 32 MiB array
+    T_big = 8192
+    assert q.q4k_mmq_workspace_bytes(T_big, 4096) > q.MMQ_NOALLOC_SCRATCH_BYTES
+    assert call(T=T_big, ldy=16) == QG_ERR_UNSUPPORTED
+    assert "static scratch" in L.qg_last_error().decode()
+    assert call(dsc=None) == QG_ERR_NULL_POINTER
+    assert call(K=300, ldx=300) == QG_ERR_BAD_SHAPE
+    assert call(T=0) == QG_OK and call(N=0) == QG_OK

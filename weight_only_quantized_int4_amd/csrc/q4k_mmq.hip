@@ -31,8 +31,20 @@
 // matrix cores (v_mfma_f32_16x16x4f32, four chunks per instruction) into
 // accumulators of its own, added at the end.  Vector-ALU issue is the limit of
 // this kernel; both moves take work off it (measured 3-11% faster each).
+#include <mutex>
+
+#include "qgemv.h"
 #include "qgemv_device.h"
 #include "qgemv_launch.h"
+
+// Workspace of the prefill entry point that allocates nothing
+// (qgemm_q4k_mmq_noalloc): the 8-bit codes and activation scales live in this
+// file-scope device array instead of a caller-owned buffer.  Every GPU the
+// library runs on holds its own copy, from the library's load until the
+// process ends.  Host code must never pass the array's name to a kernel (on
+// the host it is a stand-in, not a device address); it uses the address that
+// hipGetSymbolAddress returns for the current device (mmq_static_scratch).
+static __device__ __align__(256) uint8_t scratch[QG_MMQ_NOALLOC_SCRATCH_BYTES];
 
 namespace qg {
 namespace {
@@ -310,6 +322,28 @@ hipError_t launch_mmq_wt(const int8_t* qa, const float2* sda, const uint8_t* w, 
 }
 
 }  // namespace
+
+hipError_t mmq_static_scratch(void** ptr) {
+  // Looked up once per device, with that device current; kept per device
+  // (each GPU has the array at an address of its own).
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t q8_workspace_codes_bytes(int64_t T, int64_t K) {
   return ((size_t)T * (size_t)K + 255) & ~(size_t)255;

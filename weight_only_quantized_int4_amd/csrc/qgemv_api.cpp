@@ -302,11 +302,10 @@ qg_status q8_quantize_rows(const float* x, int64_t ldx, int8_t* qa, float* sda, 
                     fn);
 }
 
-qg_status qgemm_q4k_mmq(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
-                        int64_t ldy, int64_t T, int64_t N, int64_t K, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  begin_call();
-  static const char fn[] = "qgemm_q4k_mmq";
+static qg_status mmq_common(const char* fn, const float* x, int64_t ldx, const uint8_t* w,
+                            const float* dsc, float* y, int64_t ldy, int64_t T, int64_t N,
+                            int64_t K, void* workspace, size_t workspace_bytes, bool static_ws,
+                            void* stream) {
   if (!x || !w || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, w and y are required", fn);
   if (!dsc) return fail(QG_ERR_NULL_POINTER, "%s: dsc plane is NULL (no silent fallback)", fn);
   if (T < 0 || N < 0 || K < 256 || K % 256 != 0)
@@ -318,18 +317,32 @@ qg_status qgemm_q4k_mmq(const float* x, int64_t ldx, const uint8_t* w, const flo
   if (qg_status s = check_ld(fn, "ldx", ldx, K)) return s;
   if (qg_status s = check_ld(fn, "ldy", ldy, N)) return s;
   if (T == 0 || N == 0) return ok();
-  if (!workspace) return fail(QG_ERR_NULL_POINTER, "%s: workspace is required", fn);
   const size_t need = q4k_mmq_workspace_bytes(T, K);
-  if (workspace_bytes < need)
-    return fail(QG_ERR_BAD_SHAPE, "%s: workspace of %zu bytes, need %zu (q4k_mmq_workspace_bytes)", fn,
-                workspace_bytes, need);
+  if (static_ws) {
+    if (need > (size_t)QG_MMQ_NOALLOC_SCRATCH_BYTES)
+      return fail(QG_ERR_UNSUPPORTED,
+                  "%s: T = %lld rows of K = %lld need %zu bytes of workspace, the static scratch "
+                  "holds %zu (use qgemm_q4k_mmq with a workspace)",
+                  fn, (long long)T, (long long)K, need, (size_t)QG_MMQ_NOALLOC_SCRATCH_BYTES);
+  } else {
+    if (!workspace) return fail(QG_ERR_NULL_POINTER, "%s: workspace is required", fn);
+    if (workspace_bytes < need)
+      return fail(QG_ERR_BAD_SHAPE, "%s: workspace of %zu bytes, need %zu (q4k_mmq_workspace_bytes)",
+                  fn, workspace_bytes, need);
+  }
   const int64_t wbytes = N * (K / 256) * 144;
   if (wbytes >= kMaxTensorBytes)
     return fail(QG_ERR_UNSUPPORTED, "%s: w is 4 GiB or larger (kernels use 32-bit offsets)", fn);
-  if (!aligned(w, 16) || !aligned(dsc, 16) || !aligned(workspace, 256) || !aligned(x, 4) ||
-      !aligned(y, 4))
-    return fail(QG_ERR_MISALIGNED,
-                "%s: w and dsc must be 16-byte, workspace 256-byte, x and y 4-byte aligned", fn);
+  if (!aligned(w, 16) || !aligned(dsc, 16) || !aligned(x, 4) || !aligned(y, 4))
+    return fail(QG_ERR_MISALIGNED, "%s: w and dsc must be 16-byte, x and y 4-byte aligned", fn);
+  if (static_ws) {
+    // The first call on a device looks the array's address up (no
+    // allocation); later calls reuse it.
+    const hipError_t e = qg::mmq_static_scratch(&workspace);
+    if (e != hipSuccess) return hip_status(e, fn);
+  } else if (!aligned(workspace, 256)) {
+    return fail(QG_ERR_MISALIGNED, "%s: workspace must be 256-byte aligned", fn);
+  }
   const Range rx = range_of(x, ((T - 1) * ldx + K) * 4), rw = range_of(w, wbytes),
               rd = range_of(dsc, N * K / 4), rws = range_of(workspace, (int64_t)need),
               ry = range_of(y, ((T - 1) * ldy + N) * 4);
@@ -344,6 +357,22 @@ qg_status qgemm_q4k_mmq(const float* x, int64_t ldx, const uint8_t* w, const flo
   const hipError_t e = qg::launch_q8_quantize(x, ldx, qa, sda, (int)T, (int)K, st);
   if (e != hipSuccess) return hip_status(e, fn);
   return hip_status(qg::launch_q4k_mmq(qa, sda, w, dsc, y, ldy, (int)T, (int)N, (int)K, st), fn);
+}
+
+qg_status qgemm_q4k_mmq(const float* x, int64_t ldx, const uint8_t* w, const float* dsc, float* y,
+                        int64_t ldy, int64_t T, int64_t N, int64_t K, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  begin_call();
+  return mmq_common("qgemm_q4k_mmq", x, ldx, w, dsc, y, ldy, T, N, K, workspace, workspace_bytes,
+                    false, stream);
+}
+
+qg_status qgemm_q4k_mmq_noalloc(const float* x, int64_t ldx, const uint8_t* w, const float* dsc,
+                                float* y, int64_t ldy, int64_t T, int64_t N, int64_t K,
+                                void* stream) {
+  begin_call();
+  return mmq_common("qgemm_q4k_mmq_noalloc", x, ldx, w, dsc, y, ldy, T, N, K, nullptr, 0, true,
+                    stream);
 }
 
 }  // extern "C"

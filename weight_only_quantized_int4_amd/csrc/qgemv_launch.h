@@ -56,6 +56,10 @@ hipError_t launch_q8_quantize(const float* x, int64_t ldx, int8_t* qa, float* sd
                               hipStream_t stream);
 hipError_t launch_q4k_mmq(const int8_t* qa, const float* sda, const uint8_t* w, const float* dsc,
                           float* y, int64_t ldy, int T, int N, int K, hipStream_t stream);
+// Device address of the static workspace of qgemm_q4k_mmq_noalloc on the
+// current device (QG_MMQ_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned),
+// looked up on the first call per device; allocates nothing.
+hipError_t mmq_static_scratch(void** ptr);
 
 hipError_t launch_bf16_gemv(const uint16_t* x, int64_t ldx, const uint16_t* w,
                             int64_t ldw, void* y, int64_t ldy, int y_type, int M,

@@ -25,6 +25,9 @@ _LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 QG_F16, QG_BF16, QG_F32 = 0, 1, 2
 _OUT_TYPES = {torch.float16: QG_F16, torch.bfloat16: QG_BF16, torch.float32: QG_F32}
 _X_TYPES = {torch.float16: QG_F16, torch.bfloat16: QG_BF16}
+# Size of the static device workspace of qgemm_q4k_mmq_noalloc
+# (QG_MMQ_NOALLOC_SCRATCH_BYTES in include/qgemv.h).
+MMQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class QgemvError(RuntimeError):
@@ -70,6 +73,7 @@ def load_library() -> ctypes.CDLL:
         "q4k_mmq_workspace_bytes": (ctypes.c_size_t, [I64, I64]),
         "q8_quantize_rows": (St, [P, I64, P, P, I64, I64, P]),
         "qgemm_q4k_mmq": (St, [P, I64, P, P, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]),
+        "qgemm_q4k_mmq_noalloc": (St, [P, I64, P, P, P, I64, I64, I64, I64, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -276,6 +280,24 @@ def qgemm_q4k_mmq(x: torch.Tensor, w: torch.Tensor, dsc: Optional[torch.Tensor],
     _check("qgemm_q4k_mmq", load_library().qgemm_q4k_mmq(
         _ptr(x), _ld(x), _ptr(w), _ptr(dsc), _ptr(y), _ld(y), T, N, K, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
+
+
+def qgemm_q4k_mmq_noalloc(x: torch.Tensor, w: torch.Tensor, dsc: Optional[torch.Tensor],
+                          y: torch.Tensor, stream=None) -> torch.Tensor:
+    """The q4_K prefill product with the workspace in the library's static
+    device array (no allocation anywhere; at most MMQ_NOALLOC_SCRATCH_BYTES of
+    workspace, see q4k_mmq_workspace_bytes).  Calls that overlap on one GPU
+    share that array and race."""
+    for t, n, d in ((x, "x", _F32), (w, "w", _U8), (dsc, "dsc", _F32), (y, "y", _F32)):
+        _arg(t, n, d)
+    N = _q4k_rows(w)
+    T, K = _xy(x, y, N)
+    if K % 256 == 0:  # otherwise the library rejects the call
+        _dense(w, "w", (N, K // 256 * 144))
+        _dense(dsc, "dsc", (K // 32 * N, 2))
+    _check("qgemm_q4k_mmq_noalloc", load_library().qgemm_q4k_mmq_noalloc(
+        _ptr(x), _ld(x), _ptr(w), _ptr(dsc), _ptr(y), _ld(y), T, N, K, _stream(stream)))
     return y
 
 
