@@ -44,10 +44,6 @@ namespace {
 
 constexpr int kQ4kBlockBytes = 144;
 
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
 // (sc, m) of chunks 2g and 2g+1 from the twelve packed bytes (words A = bytes
 // 0..3, B = 4..7, C = 8..11), as two bytes each: s2 = sc(2g) | sc(2g+1) << 8.
 // get_scale_min_k4, branch-free over the lane's g:
@@ -96,39 +92,43 @@ __device__ __forceinline__ void piece_coeffs(const Q4kPiece& cur, int g, float& 
   }
 }
 
-// acc[m] += sum over the piece's 64 weights of w * x[m, k].  xa points at the
-// staged x of chunk 2g (row stride XSTR floats; chunk 2g+1 follows at +32).
-// Word t of the 32 quant bytes holds bytes 4t..4t+3: their low nibbles are
-// elements 4t..4t+3 of chunk 2g, their high nibbles those of chunk 2g+1.
-// Each weight is w = RN(dv*q + mv) (v_fma_mix_f32 on the exact fp16 quant);
-// the two chunks accumulate into separate registers (two dependency chains).
-template <int M>
-__device__ __forceinline__ void piece_mac(const Q4kPiece& cur, const float* xa, int XSTR,
+// acc[m] += sum over NW words of quants of w * x[m, k].  Word t holds four
+// quant bytes: their low nibbles are four consecutive elements of chunk 2g at
+// xa[4t .. 4t+3], their high nibbles the same elements of chunk 2g+1 at
+// xa[32 + 4t ..] (xa: staged x of row 0 of x; row m at + m * XSTR).
+// Each weight is w = RN(dv*q + mv), exactly the definition: a nibble masked
+// into the low bits of a zero binary16 is the subnormal q * 2^-24 (exact),
+// and v_fma_mix_f32 with dv * 2^24 (an exact power-of-two scaling of dv)
+// multiplies it back to dv*q inside the fused multiply-add, whose one
+// rounding is that of dv*q + mv.  A nibble in bits 4..7 is 16q * 2^-24 and
+// takes dv * 2^20.  So the unpack is one AND per pair of weights (no bias
+// to subtract).  The two chunks accumulate into separate registers (two
+// dependency chains).
+template <int M, int NW>
+__device__ __forceinline__ void words_mac(const uint32_t (&words)[NW], const float* xa, int XSTR,
                                           float dva, float mva, float dvb, float mvb,
-                                          uint32_t magic, float (&acc_a)[M], float (&acc_b)[M]) {
-  const f16x2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  const f16x2 m64 = {(_Float16)-64.0f, (_Float16)-64.0f};
-  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+                                          float (&acc_a)[M], float (&acc_b)[M]) {
+  const float dva_lo = dva * 0x1p24f;  // chunk 2g: low nibbles
+  const float dvb_hi = dvb * 0x1p20f;  // chunk 2g+1: high nibbles
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const uint32_t word = t < 4 ? word_of(cur.q0, t) : word_of(cur.q1, t - 4);
+  for (int t = 0; t < NW; ++t) {
+    const uint32_t word = words[t];
     const uint32_t w8 = word >> 8;
-    // exact fp16 quants: A = elements (4t, 4t+2) and C = (4t+1, 4t+3) of
-    // chunk 2g; B and D the same elements of chunk 2g+1
-    const f16x2 A = bitcast<f16x2>((word & 0x000F000Fu) | magic) + m1024;
-    const f16x2 C = bitcast<f16x2>((w8 & 0x000F000Fu) | magic) + m1024;
-    const f16x2 B =
-        __builtin_elementwise_fma(bitcast<f16x2>((word & 0x00F000F0u) | magic), sixteenth, m64);
-    const f16x2 D =
-        __builtin_elementwise_fma(bitcast<f16x2>((w8 & 0x00F000F0u) | magic), sixteenth, m64);
-    const float wa0 = __builtin_fmaf((float)A.x, dva, mva);
-    const float wa1 = __builtin_fmaf((float)C.x, dva, mva);
-    const float wa2 = __builtin_fmaf((float)A.y, dva, mva);
-    const float wa3 = __builtin_fmaf((float)C.y, dva, mva);
-    const float wb0 = __builtin_fmaf((float)B.x, dvb, mvb);
-    const float wb1 = __builtin_fmaf((float)D.x, dvb, mvb);
-    const float wb2 = __builtin_fmaf((float)B.y, dvb, mvb);
-    const float wb3 = __builtin_fmaf((float)D.y, dvb, mvb);
+    // subnormal fp16 quants: A = elements (4t, 4t+2) and C = (4t+1, 4t+3) of
+    // chunk 2g (low nibbles); B and D the same elements of chunk 2g+1 (high
+    // nibbles, 16x)
+    const f16x2 A = bitcast<f16x2>(word & 0x000F000Fu);
+    const f16x2 C = bitcast<f16x2>(w8 & 0x000F000Fu);
+    const f16x2 B = bitcast<f16x2>(word & 0x00F000F0u);
+    const f16x2 D = bitcast<f16x2>(w8 & 0x00F000F0u);
+    const float wa0 = __builtin_fmaf((float)A.x, dva_lo, mva);
+    const float wa1 = __builtin_fmaf((float)C.x, dva_lo, mva);
+    const float wa2 = __builtin_fmaf((float)A.y, dva_lo, mva);
+    const float wa3 = __builtin_fmaf((float)C.y, dva_lo, mva);
+    const float wb0 = __builtin_fmaf((float)B.x, dvb_hi, mvb);
+    const float wb1 = __builtin_fmaf((float)D.x, dvb_hi, mvb);
+    const float wb2 = __builtin_fmaf((float)B.y, dvb_hi, mvb);
+    const float wb3 = __builtin_fmaf((float)D.y, dvb_hi, mvb);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const float4 xa4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 4 * t);
@@ -146,6 +146,16 @@ __device__ __forceinline__ void piece_mac(const Q4kPiece& cur, const float* xa, 
       acc_b[m] = v;
     }
   }
+}
+
+// The 64 weights of a piece (32 quant bytes of pair g: chunks 2g and 2g+1).
+template <int M>
+__device__ __forceinline__ void piece_mac(const Q4kPiece& cur, const float* xa, int XSTR,
+                                          float dva, float mva, float dvb, float mvb,
+                                          float (&acc_a)[M], float (&acc_b)[M]) {
+  const uint32_t words[8] = {cur.q0.x, cur.q0.y, cur.q0.z, cur.q0.w,
+                             cur.q1.x, cur.q1.y, cur.q1.z, cur.q1.w};
+  words_mac<M, 8>(words, xa, XSTR, dva, mva, dvb, mvb, acc_a, acc_b);
 }
 
 template <int M, int LPR, int NT, bool DSC>
@@ -169,7 +179,6 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
   const int nsb = K >> 8;
   const uint32_t wo = nl * (uint32_t)nsb * (uint32_t)kQ4kBlockBytes;
 
-  const uint32_t magic = vreg_const(0x64006400u);
 
   auto load = [&](Q4kPiece& st, int sb) {
     const uint32_t bo = wo + (uint32_t)sb * kQ4kBlockBytes;
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
 
       float dva, mva, dvb, mvb;
       piece_coeffs<DSC>(cur, g, dva, mva, dvb, mvb);
-      piece_mac<M>(cur, xs + p * 68, XSTR, dva, mva, dvb, mvb, magic, acc_a, acc_b);
+      piece_mac<M>(cur, xs + p * 68, XSTR, dva, mva, dvb, mvb, acc_a, acc_b);
       if (more) cur = nxt;
     }
   }
@@ -252,17 +261,28 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
 // register ring of D items that crosses row boundaries.
 // M = 1 with 1024-thread workgroups and a ring of at most 2 items asks for 64
 // VGPRs (8 wavefronts per SIMD), so that two workgroups share a CU.
-template <int M, int NT, bool DSC, bool STRIDED, int D>
+// PL (with DSC and contiguous row ranges): the workgroup stages the plane
+// entries of its own rows in LDS next to x, as [row][chunk] float2.  In the
+// global plane the entries of one chunk for consecutive rows are adjacent,
+// so the staging loads read whole 128-byte lines; a lane's one-row-per-
+// wavefront access (its two chunks of one row, N * 8 bytes apart) then comes
+// from LDS as one 16-byte read.  Each thread loads at most kPlaneSlots
+// entries, all issued between the x loads and the first weight loads.
+constexpr int kPlaneSlots = 8;
+
+template <int M, int NT, bool DSC, bool STRIDED, int D, bool PL = false>
 __global__ __launch_bounds__(NT)
 __attribute__((amdgpu_waves_per_eu(M == 1 && NT == 1024 && D <= 2 ? 8 : 1)))
 void q4k_gemv_persistent(
     const float* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const float2* __restrict__ dsc, float* __restrict__ y, int64_t ldy, int N, int K,
     int x_vec16) {
+  static_assert(!PL || (DSC && !STRIDED), "the plane tile needs the plane and contiguous rows");
   constexpr int NW = NT / kWave;  // wavefronts (rows in flight) per workgroup
   extern __shared__ float smem[];
   const int XSTR = (K >> 6) * 68;  // floats per x row in LDS (64 + 4 pad per piece)
   float* xs = smem;                // [M][K/64][68]
+  float* ptile = smem + M * XSTR;  // PL: [rows of the workgroup][K/32][2]
   const int tid = threadIdx.x;
   const int wv = tid / kWave;
   const int j = tid % kWave;
@@ -282,7 +302,6 @@ void q4k_gemv_persistent(
   const int nrows = span > 0 ? (span + rstep - 1) / rstep : 0;  // rows of this wavefront
   const int nitems = nrows * PPI;
 
-  const uint32_t magic = vreg_const(0x64006400u);
 
   auto load = [&](Q4kPiece& st, int row, int it) {
     row = row < N ? row : N - 1;  // a bound only: loaded items never pass the last row
@@ -292,11 +311,11 @@ void q4k_gemv_persistent(
     const uint32_t bo = ((uint32_t)row * (uint32_t)nsb + sb) * (uint32_t)kQ4kBlockBytes;
     st.q0 = load16(w + (bo + 16u + 32u * g));
     st.q1 = load16(w + (bo + 32u + 32u * g));
-    if constexpr (DSC) {
+    if constexpr (DSC && !PL) {
       const uint32_t c = sb * 8u + 2u * g;
       st.ea = load8f(dsc + (c * (uint32_t)N + (uint32_t)row));
       st.eb = load8f(dsc + ((c + 1u) * (uint32_t)N + (uint32_t)row));
-    } else {
+    } else if constexpr (!DSC) {
       st.h = load16(w + bo);
     }
   };
@@ -323,6 +342,42 @@ void q4k_gemv_persistent(
   // behind the weight stream of the whole grid, x would arrive late (measured
   // 0.2-0.5 us per call on the 7B layer shapes).  With the plane, the ring's
   // first loads go out right behind the x loads (measured better there).
+  // Plane tile (PL): entry e = c * R + r (chunk c, row r_begin + r) is read
+  // from the plane in that order (consecutive lanes, consecutive rows of one
+  // chunk) and stored at ptile[(r * C + c) * 2].  The host guarantees
+  // R * C <= NT * kPlaneSlots.  e / R through a binary32 reciprocal: exact
+  // for e < 2^22 (the quotient is never closer than 0.5 / R to an integer).
+  const int C = K >> 5;
+  const int R = r_end - r_begin;
+  float2 pv[PL ? kPlaneSlots : 1];
+  auto plane_load = [&] {
+    if constexpr (PL) {
+      const float rinv = 1.0f / (float)R;
+#pragma unroll
+      for (int k = 0; k < kPlaneSlots; ++k) {
+        int e = tid + k * NT;
+        e = e < R * C ? e : R * C - 1;
+        const int c = (int)(((float)e + 0.5f) * rinv);
+        const int r = e - c * R;
+        pv[k] = load8f(dsc + ((uint32_t)c * (uint32_t)N + (uint32_t)(r_begin + r)));
+      }
+    }
+  };
+  auto plane_store = [&] {
+    if constexpr (PL) {
+      const float rinv = 1.0f / (float)R;
+#pragma unroll
+      for (int k = 0; k < kPlaneSlots; ++k) {
+        const int e = tid + k * NT;
+        if (e < R * C) {
+          const int c = (int)(((float)e + 0.5f) * rinv);
+          const int r = e - c * R;
+          *reinterpret_cast<float2*>(ptile + 2 * (r * C + c)) = pv[k];
+        }
+      }
+    }
+  };
+
   if (x_vec16) {
     const int v4 = K >> 2;
     stage_slots<2>(
@@ -337,19 +392,23 @@ void q4k_gemv_persistent(
           *reinterpret_cast<uint4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) = u;
         },
         [&] {
+          plane_load();
           if constexpr (DSC) fill_ring();
         });
     if constexpr (!DSC) {
       __builtin_amdgcn_sched_barrier(0);
       fill_ring();
     }
+    plane_store();
     __syncthreads();
   } else {
+    plane_load();
     fill_ring();
     for (int t = tid; t < M * K; t += NT) {
       const int m = t / K, i = t - m * K;
       xs[m * XSTR + (i >> 6) * 68 + (i & 63)] = x[m * ldx + i];
     }
+    plane_store();
     __syncthreads();
   }
 
@@ -361,8 +420,14 @@ void q4k_gemv_persistent(
     const int p = j + kWave * it;
     if (p < P) {
       float dva, mva, dvb, mvb;
-      piece_coeffs<DSC>(cur, g, dva, mva, dvb, mvb);
-      piece_mac<M>(cur, xs + p * 68, XSTR, dva, mva, dvb, mvb, magic, acc_a, acc_b);
+      if constexpr (PL) {
+        // chunks 2p and 2p + 1 of this row: adjacent in the tile
+        const float4 e4 = *reinterpret_cast<const float4*>(ptile + 4 * ((row - r_begin) * (C >> 1) + p));
+        dva = e4.x; mva = e4.y; dvb = e4.z; mvb = e4.w;
+      } else {
+        piece_coeffs<DSC>(cur, g, dva, mva, dvb, mvb);
+      }
+      piece_mac<M>(cur, xs + p * 68, XSTR, dva, mva, dvb, mvb, acc_a, acc_b);
     }
     if (it == PPI - 1) {  // row finished (uniform across the wavefront)
 #pragma unroll
@@ -432,7 +497,9 @@ constexpr bool kQ4kStrided = false;
 
 // One persistent launch with a ring of D items per lane: each wavefront gets
 // D / PPI rows (at least one), so that all of its items can be in flight at
-// once; the grid is capped at one resident round.
+// once; the grid is capped at one resident round.  With the plane, the
+// workgroup's plane tile goes to LDS whenever it fits (rows * chunks at most
+// NT * kPlaneSlots entries, and x plus the tile within the LDS limit).
 template <int M, int NT, int D>
 hipError_t launch_persistent(const float* x, int64_t ldx, const uint8_t* w, const float2* dsc2,
                              float* y, int64_t ldy, int N, int K, int x_vec16, size_t full, int PPI,
@@ -445,7 +512,30 @@ hipError_t launch_persistent(const float* x, int64_t ldx, const uint8_t* w, cons
   const int rows_per_wave = D / PPI > 1 ? D / PPI : 1;
   const int rows_per_wg = (NT / kWave) * rows_per_wave;
   const int want = (N + rows_per_wg - 1) / rows_per_wg;
-  const int grid = want < cap ? want : cap;
+  int grid = want < cap ? want : cap;
+  if constexpr (!kQ4kStrided) {
+    if (dsc2) {
+      auto kern_pl = q4k_gemv_persistent<M, NT, true, false, D, true>;
+      const int64_t C = K / 32;
+      int g = grid;
+      for (int pass = 0; pass < 2; ++pass) {  // the tile's LDS may lower the resident count
+        const int64_t R = ((int64_t)N + g - 1) / g;
+        const size_t lds = full + (size_t)(R * C) * 8;
+        if (R * C > (int64_t)NT * kPlaneSlots || lds > (size_t)kLdsMax) break;
+        const hipError_t e2 = allow_lds(kern_pl, lds);
+        if (e2 != hipSuccess) return e2;
+        const int cap_pl = resident_workgroups(kern_pl, NT, lds);
+        const int g2 = want < cap_pl ? want : cap_pl;
+        if (g2 >= g) {  // the tile fits this grid: launch
+          hipLaunchKernelGGL(kern_pl, dim3(g), dim3(NT), lds, stream, x, ldx, w, dsc2, y, ldy, N,
+                             K, x_vec16);
+          note_launch(kPathQ4kPersistentPlane, M, g, NT, lds);
+          return hipGetLastError();
+        }
+        g = g2;
+      }
+    }
+  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), full, stream, x, ldx, w, dsc2, y, ldy, N, K,
                      x_vec16);
   note_launch(dsc2 ? kPathQ4kPersistentPlane : kPathQ4kPersistent, M, grid, NT, full);

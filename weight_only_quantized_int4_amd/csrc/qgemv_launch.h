@@ -29,7 +29,7 @@ enum Path : int {
   kPathBf16General,
   kPathQ8Quantize,
   kPathQ4kMmq,
-  kPathCount
+    kPathCount
 };
 
 // Record one launch: counted for `path` and appended to the calling thread's
