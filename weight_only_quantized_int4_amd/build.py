@@ -1,8 +1,10 @@
 """Build libqgemv.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
 Each source is compiled to an object under ``_build/`` (in parallel), then the
-objects are linked into ``weight_only_quantized_int4_amd/libqgemv.so``.  hipcc
-cross-compiles for gfx950 without a GPU.
+objects are linked into ``weight_only_quantized_int4_amd/libqgemv.so``.  The
+bench's streaming-read probe (``read_probe.hip``) is linked into a library of
+its own, ``libqgemv_readprobe.so``, so the product library never holds it.
+hipcc cross-compiles for gfx950 without a GPU.
 """
 from __future__ import annotations
 
@@ -17,9 +19,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqgemv.so")
+PROBE_LIB = os.path.join(PKG, "libqgemv_readprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["qgemv_api.cpp", "int4_gemv.hip", "q4k_gemv.hip", "bf16_gemv.hip", "q4k_mmq.hip"]
+PROBE_SOURCES = ["read_probe.hip"]
 
 # -packed-fp32-ops: never emit v_pk_{add,mul,fma}_f32 (kept off on this target).
 # Correctly rounded binary32 division: the 8-bit activation codes are decided
@@ -48,19 +52,28 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
+def _link(objs, out: str) -> None:
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+
+
+def build(extra_flags=(), out: str = LIB, verbose: bool = False, probe: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + (PROBE_SOURCES if probe else [])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra_flags)), srcs)))
+    _link([objs[s] for s in SOURCES], out)
     _write_build_info(out)
     if verbose:
         print(f"built {out}")
+    if probe:
+        _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
+        if verbose:
+            print(f"built {PROBE_LIB}")
     return out
 
 

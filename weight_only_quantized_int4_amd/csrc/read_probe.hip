@@ -1,0 +1,119 @@
+// read_probe.hip -- streaming-read kernels that measure how fast this GPU
+// reads a buffer of a given size from HBM.  Bench-only: built into its own
+// library (libqgemv_readprobe.so), never into libqgemv.so.
+//
+// The decode GEMV kernels are bounded by how fast their weight bytes can be
+// read.  These kernels read the same number of bytes and do nothing else, so
+// their time is the floor a GEMV of that size is compared against.  The
+// question of the onnx-genai pull request #1000 ("What it does", the ncu
+// table) -- does an asynchronous copy into on-chip memory (cp.async with an
+// evict-first hint) stream faster than plain loads into registers? -- is asked
+// here of gfx950's analogues:
+//   variant 0: plain 16-byte loads into registers (cached);
+//   variant 1: 16-byte non-temporal loads into registers (the streaming hint);
+//   variant 2: 16-byte LDS-DMA loads (global_load_lds_dwordx4: HBM -> LDS
+//              without passing through registers, the gfx950 counterpart
+//              of cp.async), each wave's data read back from LDS.
+// Every thread keeps kInFlight loads outstanding, over a grid-stride loop in
+// which consecutive lanes read consecutive 16-byte words (each wavefront
+// instruction reads 1 KB of contiguous memory).  The words are XOR-folded
+// and the fold is stored only when it equals a constant, so no load can be
+// removed and the kernel writes (almost) nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kInFlight = 4;
+constexpr uint32_t kNever = 0x9E3779B9u;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int V>
+__device__ __forceinline__ u32x4 load_word(const u32x4* p) {
+  if constexpr (V == 1) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <int V>
+__global__ __launch_bounds__(kThreads) void read_regs(const u32x4* __restrict__ src, uint64_t n16,
+                                                      uint32_t* __restrict__ sink) {
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kInFlight - 1) * stride < n16; i += kInFlight * stride) {
+    u32x4 v[kInFlight];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) v[u] = load_word<V>(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = load_word<V>(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == kNever) sink[0] = acc;
+}
+
+// LDS-DMA: each wavefront owns kInFlight slots of 1 KB (64 lanes x 16 bytes)
+// in LDS.  A round issues kInFlight DMA loads, waits for them, and each lane
+// folds one word of its slot; the barrier-free reuse of a slot is safe because
+// a lane's own LDS read completes before the lane issues the next round.
+__global__ __launch_bounds__(kThreads) void read_lds_dma(const u32x4* __restrict__ src,
+                                                         uint64_t n16,
+                                                         uint32_t* __restrict__ sink) {
+  __shared__ u32x4 slots[kThreads / 64][kInFlight][64];
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i < n16; i += kInFlight * stride) {
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      uint64_t e = i + u * stride;
+      e = e < n16 ? e : n16 - 1;  // lanes past the end re-read the last word
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src + e),
+          (__attribute__((address_space(3))) void*)&slots[wave][u][0], 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0), lgkmcnt(0): the DMA data is in LDS
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      const u32x4 v = slots[wave][u][lane];
+      acc ^= v.x ^ v.w;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the slot reads are done before the next DMA
+  }
+  if (acc == kNever) sink[0] = acc;
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+// Read `bytes` bytes at `src` (device memory, 16-byte aligned, a multiple of
+// 16 bytes) with variant 0, 1 or 2 on `grid` workgroups of 256 threads,
+// enqueued on `stream`.  `sink` is a device word written only in the
+// (practically impossible) case that the fold equals a fixed constant.
+// Returns 0 on success, -1 on a bad argument, or the HIP error code.
+int qg_read_probe(const void* src, uint64_t bytes, int variant, int grid, uint32_t* sink,
+                  void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(src) % 16 != 0 || grid < 1 || variant < 0 || variant > 2)
+    return -1;
+  const u32x4* s = static_cast<const u32x4*>(src);
+  const uint64_t n16 = bytes / 16;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (variant == 0)
+    hipLaunchKernelGGL(read_regs<0>, dim3(grid), dim3(kThreads), 0, st, s, n16, sink);
+  else if (variant == 1)
+    hipLaunchKernelGGL(read_regs<1>, dim3(grid), dim3(kThreads), 0, st, s, n16, sink);
+  else
+    hipLaunchKernelGGL(read_lds_dma, dim3(grid), dim3(kThreads), 0, st, s, n16, sink);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"
+#pragma GCC visibility pop
