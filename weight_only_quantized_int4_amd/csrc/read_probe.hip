@@ -13,9 +13,12 @@
 //   variant 1: 16-byte non-temporal loads into registers (the streaming hint);
 //   variant 2: 16-byte LDS-DMA loads (global_load_lds_dwordx4: HBM -> LDS
 //              without passing through registers, the gfx950 counterpart
-//              of cp.async), each wave's data read back from LDS.
-// Every thread keeps kInFlight loads outstanding, over a grid-stride loop in
-// which consecutive lanes read consecutive 16-byte words (each wavefront
+//              of cp.async), each wave's data read back from LDS;
+//   variant 3: as 1 with 8 loads in flight per thread;
+//   variant 4: as 1, but each wavefront reads one contiguous 4 KB span per
+//              round (4 loads 1 KB apart) instead of the grid-wide stride.
+// Variants 0-3 keep their loads outstanding over a grid-stride loop in which
+// consecutive lanes read consecutive 16-byte words (each wavefront
 // instruction reads 1 KB of contiguous memory).  The words are XOR-folded
 // and the fold is stored only when it equals a constant, so no load can be
 // removed and the kernel writes (almost) nothing.
@@ -36,22 +39,47 @@ __device__ __forceinline__ u32x4 load_word(const u32x4* p) {
   return *p;
 }
 
-template <int V>
+template <int V, int F>
 __global__ __launch_bounds__(kThreads) void read_regs(const u32x4* __restrict__ src, uint64_t n16,
                                                       uint32_t* __restrict__ sink) {
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + (kInFlight - 1) * stride < n16; i += kInFlight * stride) {
-    u32x4 v[kInFlight];
+  for (; i + (F - 1) * stride < n16; i += F * stride) {
+    u32x4 v[F];
 #pragma unroll
-    for (int u = 0; u < kInFlight; ++u) v[u] = load_word<V>(src + i + u * stride);
+    for (int u = 0; u < F; ++u) v[u] = load_word<V>(src + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < kInFlight; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < F; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
     const u32x4 v = load_word<V>(src + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == kNever) sink[0] = acc;
+}
+
+// Wavefront-contiguous spans: global wavefront gw reads spans gw, gw + GW,
+// ... of 4 KB (GW = all wavefronts), each as kInFlight non-temporal loads
+// 1 KB apart (lane l at +16 l).
+__global__ __launch_bounds__(kThreads) void read_spans(const u32x4* __restrict__ src, uint64_t n16,
+                                                       uint32_t* __restrict__ sink) {
+  constexpr uint64_t kSpan = 64 * kInFlight;  // 16-byte words per span
+  const uint64_t gw = (uint64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+  const uint64_t nw = (uint64_t)gridDim.x * (kThreads / 64);
+  const uint32_t lane = threadIdx.x % 64;
+  uint32_t acc = 0;
+  for (uint64_t sp = gw; sp * kSpan < n16; sp += nw) {
+    const uint64_t base = sp * kSpan + lane;
+    u32x4 v[kInFlight];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      uint64_t e = base + 64 * u;
+      e = e < n16 ? e : n16 - 1;
+      v[u] = __builtin_nontemporal_load(src + e);
+    }
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   if (acc == kNever) sink[0] = acc;
 }
@@ -94,24 +122,29 @@ __global__ __launch_bounds__(kThreads) void read_lds_dma(const u32x4* __restrict
 extern "C" {
 
 // Read `bytes` bytes at `src` (device memory, 16-byte aligned, a multiple of
-// 16 bytes) with variant 0, 1 or 2 on `grid` workgroups of 256 threads,
+// 16 bytes) with variant 0..4 on `grid` workgroups of 256 threads,
 // enqueued on `stream`.  `sink` is a device word written only in the
 // (practically impossible) case that the fold equals a fixed constant.
 // Returns 0 on success, -1 on a bad argument, or the HIP error code.
 int qg_read_probe(const void* src, uint64_t bytes, int variant, int grid, uint32_t* sink,
                   void* stream) {
   if (!src || !sink || bytes == 0 || bytes % 16 != 0 ||
-      reinterpret_cast<uintptr_t>(src) % 16 != 0 || grid < 1 || variant < 0 || variant > 2)
+      reinterpret_cast<uintptr_t>(src) % 16 != 0 || grid < 1 || variant < 0 || variant > 4)
     return -1;
   const u32x4* s = static_cast<const u32x4*>(src);
   const uint64_t n16 = bytes / 16;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (variant == 0)
-    hipLaunchKernelGGL(read_regs<0>, dim3(grid), dim3(kThreads), 0, st, s, n16, sink);
+    hipLaunchKernelGGL((read_regs<0, kInFlight>), dim3(grid), dim3(kThreads), 0, st, s, n16, sink);
   else if (variant == 1)
-    hipLaunchKernelGGL(read_regs<1>, dim3(grid), dim3(kThreads), 0, st, s, n16, sink);
-  else
+    hipLaunchKernelGGL((read_regs<1, kInFlight>), dim3(grid), dim3(kThreads), 0, st, s, n16, sink);
+  else if (variant == 2)
     hipLaunchKernelGGL(read_lds_dma, dim3(grid), dim3(kThreads), 0, st, s, n16, sink);
+  else if (variant == 3)
+    hipLaunchKernelGGL((read_regs<1, 2 * kInFlight>), dim3(grid), dim3(kThreads), 0, st, s, n16,
+                       sink);
+  else
+    hipLaunchKernelGGL(read_spans, dim3(grid), dim3(kThreads), 0, st, s, n16, sink);
   return (int)hipGetLastError();
 }
 
