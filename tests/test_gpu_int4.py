@@ -332,6 +332,59 @@ def test_layer_shapes_single_row_sampled(N, K, bs, asym):
     assert_accept(y[:, list(cols)], yr[:1], S[:1], "f32", f"int4 layer {N}x{K} bs={bs}")
 
 
+# Rows of 2048, 4096 or 8192 weights at M = 1 take the span kernel (4 KB runs
+# of 4, 2 or 1 whole rows per wavefront): ragged last spans (N not a multiple
+# of the rows per span, down to N = 1), every block size, both zero-point
+# modes and every output type, on every column.
+@pytest.mark.parametrize("N,K,bs,asym,out_dtype", [
+    (1, 2048, 32, True, torch.float32), (3, 4096, 64, False, torch.float16),
+    (4099, 2048, 32, True, torch.bfloat16), (1001, 4096, 256, True, torch.float32),
+    (517, 8192, 128, False, torch.float16), (2, 8192, 32, True, torch.float32),
+    (9000, 4096, 32, True, torch.float16)])
+def test_span_kernel_every_column(N, K, bs, asym, out_dtype):
+    say(f"int4 span N={N} K={K} bs={bs} asym={asym} out={out_dtype}")
+    p = int4_case(N, K, bs, asym, 900 + N % 97)
+    y = y_host(_run(p, 1, out_dtype))
+    assert q.last_launch().startswith("int4_span M=1 "), q.last_launch()
+    yr, S = int4_ref(N, K, bs, asym, 900 + N % 97)
+    assert_accept(y, yr[:1], S[:1], OUT_NAME[out_dtype], f"int4 span {N}x{K} bs={bs}")
+
+
+def test_span_kernel_strided_unaligned_x_and_strided_y():
+    N, K, bs = 777, 4096, 32
+    say("int4 span strided/unaligned x, strided y")
+    p = int4_case(N, K, bs, True, 56)
+    buf = np.zeros(1 + (K + 3), dtype=np.uint16)
+    buf[1:1 + K] = p.x[0]
+    xt = f16_dev(buf)[1:].view(1, K + 3)[:, :K]
+    assert xt.data_ptr() % 16 == 2
+    y = y_host(_run(p, 1, torch.float16, x=xt, ldy=N + 3))
+    assert q.last_launch().startswith("int4_span M=1 "), q.last_launch()
+    yr, S = int4_ref(N, K, bs, True, 56)
+    assert_accept(y, yr[:1], S[:1], "f16", "int4 span strided")
+
+
+@pytest.mark.parametrize("K", [2048, 4096, 8192])
+def test_span_kernel_one_hot_is_bit_exact(K):
+    """x = e_k through the span kernel, fp32 out: y[n] equals the oracle's
+    dequantized w[n,k] bitwise, for k at the edges of each lane's pieces."""
+    N, bs = 70, 32
+    p = int4_case(N, K, bs, True, 33)
+    wdq = oracle.int4_dequant(p.w, p.scales, p.zp, N, K, bs)
+    wd, sd, zd = to_dev(p.w), f16_dev(p.scales), to_dev(p.zp)
+    ks = sorted({0, 1, 31, 32, 33, 2047, 2048 % K, 2049 % K, K // 2, K - 32, K - 1})
+    say(f"int4 span one-hot K={K}, {len(ks)} columns of x")
+    ys = torch.empty((len(ks), N), dtype=torch.float32, device=DEV)
+    for i, k in enumerate(ks):
+        x = torch.zeros((1, K), dtype=torch.float16, device=DEV)
+        x[0, k] = 1.0
+        q.qgemv_int4_blockwise(x, wd, sd, zd, ys[i:i + 1], bs)
+        assert q.last_launch().startswith("int4_span M=1 "), q.last_launch()
+    got = ys.cpu().numpy()
+    want = wdq[:, ks].T.astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
 def test_misaligned_scales_and_zero_points():
     # scales 2 bytes past an 8-byte boundary and zero points at an odd address
     N, K, bs, M = 300, 1024, 32, 4

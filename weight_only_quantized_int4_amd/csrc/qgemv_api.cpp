@@ -30,7 +30,8 @@ const char* const kPathNames[qg::kPathCount] = {
     "int4_dot2_persistent", "int4_dot2_tiled",      "int4_mfma_tiles", "int4_mfma_split",
     "int4_mfma_phased",     "q4k_persistent",       "q4k_persistent_plane", "q4k_tiled",
     "q4k_tiled_plane",      "q4k_plane_build",      "bf16_aligned",    "bf16_mfma_tiles",
-    "bf16_mfma_split",      "bf16_general",         "q8_quantize",     "q4k_mmq"};
+    "bf16_mfma_split",      "bf16_general",         "q8_quantize",     "q4k_mmq",
+    "int4_span"};
 
 void begin_call() {
   g_last_launch[0] = '\0';

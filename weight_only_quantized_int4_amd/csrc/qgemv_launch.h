@@ -29,6 +29,7 @@ enum Path : int {
   kPathBf16General,
   kPathQ8Quantize,
   kPathQ4kMmq,
+  kPathInt4Span,
     kPathCount
 };
 
