@@ -284,7 +284,7 @@ void q4k_gemv_persistent(
   float* xs = smem;                // [M][K/64][68]
   float* ptile = smem + M * XSTR;  // PL: [rows of the workgroup][K/32][2]
   const int tid = threadIdx.x;
-  const int wv = tid / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // rows are wave-uniform
   const int j = tid % kWave;
   const int g = j & 3;
   // Row order: STRIDED gives wavefront gw rows gw, gw + GW, ... (GW = all
@@ -303,20 +303,29 @@ void q4k_gemv_persistent(
   const int nitems = nrows * PPI;
 
 
+  // Item it of a row is piece j + 64 * it for lane j: 16 super-blocks past
+  // the lane's first piece.  Row offsets are scalar (the row is wave-uniform)
+  // and the lane parts are fixed, so an item's addresses cost a few VALU
+  // operations.  Lanes past the end of a ragged last item re-read their first
+  // piece (or the row's last piece when the row has fewer than 64); their
+  // sums are skipped.
+  const int pc0 = j < P ? j : P - 1;
+  const uint32_t lq0 = (uint32_t)(pc0 >> 2) * kQ4kBlockBytes + 32u * (uint32_t)g;
+  const uint32_t c0N = ((uint32_t)(pc0 >> 2) * 8u + 2u * (uint32_t)g) * (uint32_t)N;
+  const size_t row_bytes = (size_t)nsb * kQ4kBlockBytes;
   auto load = [&](Q4kPiece& st, int row, int it) {
     row = row < N ? row : N - 1;  // a bound only: loaded items never pass the last row
-    int p = j + kWave * it;
-    p = p < P ? p : P - 1;  // idle lanes of a ragged last stride re-read a valid piece
-    const uint32_t sb = (uint32_t)(p >> 2);
-    const uint32_t bo = ((uint32_t)row * (uint32_t)nsb + sb) * (uint32_t)kQ4kBlockBytes;
-    st.q0 = load16(w + (bo + 16u + 32u * g));
-    st.q1 = load16(w + (bo + 32u + 32u * g));
+    const bool live = j + kWave * it < P;
+    const uint32_t lo = live ? lq0 + (uint32_t)it * (16u * kQ4kBlockBytes) : lq0;
+    const uint8_t* rp = w + (size_t)row * row_bytes;
+    st.q0 = load16(rp + (lo + 16u));
+    st.q1 = load16(rp + (lo + 32u));
     if constexpr (DSC && !PL) {
-      const uint32_t c = sb * 8u + 2u * g;
-      st.ea = load8f(dsc + (c * (uint32_t)N + (uint32_t)row));
-      st.eb = load8f(dsc + ((c + 1u) * (uint32_t)N + (uint32_t)row));
+      const uint32_t e = (live ? c0N + (uint32_t)it * (128u * (uint32_t)N) : c0N) + (uint32_t)row;
+      st.ea = load8f(dsc + e);
+      st.eb = load8f(dsc + (e + (uint32_t)N));
     } else if constexpr (!DSC) {
-      st.h = load16(w + bo);
+      st.h = load16(rp + (lo - 32u * (uint32_t)g));
     }
   };
   auto advance = [&](int& row, int& it) {
@@ -441,21 +450,29 @@ void q4k_gemv_persistent(
 
   int prow = first, pit = 0;  // next item to consume
   int u = 0;
+  // Steady state: every consumed slot is reloaded (unconditionally, so the
+  // ring's registers are reused in place); the last 2D - 1 items at most are
+  // finished below with the reload under a (wave-uniform) bound.
 #pragma unroll 1
-  for (; u + D <= nitems; u += D) {
+  for (; u + 2 * D <= nitems; u += D) {
 #pragma unroll
     for (int k = 0; k < D; ++k) {
       consume(ring[k], prow, pit);
       advance(prow, pit);
-      if (u + k + D < nitems) load(ring[k], lrow, lit);
+      load(ring[k], lrow, lit);
       advance(lrow, lit);
     }
   }
+#pragma unroll 1
+  for (; u < nitems; u += D) {
 #pragma unroll
-  for (int k = 0; k < D; ++k) {
-    if (u + k < nitems) {
-      consume(ring[k], prow, pit);
-      advance(prow, pit);
+    for (int k = 0; k < D; ++k) {
+      if (u + k < nitems) {
+        consume(ring[k], prow, pit);
+        advance(prow, pit);
+        if (u + k + D < nitems) load(ring[k], lrow, lit);
+        advance(lrow, lit);
+      }
     }
   }
 }
@@ -555,8 +572,9 @@ hipError_t launch_m(const float* x, int64_t ldx, const uint8_t* w, const float* 
   // x as fp32, 68 floats per 64 elements.
   const size_t full = (size_t)M * (K / 64) * 68 * 4;
   if (full <= (size_t)kLdsMax) {
-    // One item per lane in flight over a full grid measured faster than
-    // deeper rings on fewer workgroups (4096 x 11008 and 11008 x 4096, M = 1).
+    // One item per lane in flight: measured faster than rings as deep as a
+    // row's items (4096 x 11008, M = 1: 9.6 against 10.4 us cold) and than
+    // deeper rings on fewer workgroups.
     return launch_persistent<M, NT, 1>(x, ldx, w, dsc2, y, ldy, N, K, x_vec16, full, 1, stream);
   }
   // The tiled kernel is launched for at most 4 rows of x (launch_q4k_gemv

@@ -1,7 +1,7 @@
 // qgemv_device.h -- device-side helpers shared by the gfx950 GEMV kernels.
 //
 // Everything here is CDNA4 code: 64-wide wavefronts, packed-f16 VOP3P math,
-// v_dot2 instructions, DPP/bpermute cross-lane reductions.
+// v_dot2 instructions, DPP and lane-swap cross-lane reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -122,17 +122,36 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
 }
 
+// v + the value of lane (lane ^ S), S = 16 or 32, in every lane: one
+// v_permlane16_swap / v_permlane32_swap (a VALU lane exchange, no LDS) and
+// one add.  The swap of v with itself leaves each lane's own value in one
+// result and its partner's in the other; their sum is the same in both lanes
+// of a pair (addition commutes).
+template <int S>
+__device__ __forceinline__ float swap_add(float v) {
+  static_assert(S == 16 || S == 32, "lane distance");
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (S == 16) {
+    const auto h = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  } else {
+    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  }
+}
+
 // Sum over aligned groups of G consecutive lanes (G a power of two <= 64);
 // every lane of the group receives the group total.  Steps inside a 16-lane
-// row use DPP (fused into v_add_f32_dpp); larger groups finish with shuffles.
+// row use DPP (fused into v_add_f32_dpp); larger groups finish with lane
+// swaps.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (G >= 2) v += dpp_f32<kDppXor1>(v);
   if constexpr (G >= 4) v += dpp_f32<kDppXor2>(v);
   if constexpr (G >= 8) v += dpp_f32<kDppHalfMirror>(v);
   if constexpr (G >= 16) v += dpp_f32<kDppMirror>(v);
-  if constexpr (G >= 32) v += __shfl_xor(v, 16, kWave);
-  if constexpr (G >= 64) v += __shfl_xor(v, 32, kWave);
+  if constexpr (G >= 32) v = swap_add<16>(v);
+  if constexpr (G >= 64) v = swap_add<32>(v);
   return v;
 }
 
