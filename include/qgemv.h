@@ -98,6 +98,78 @@ qg_status qgemv_int4_blockwise(const void *x, int64_t ldx, int32_t x_type,
                                int32_t block_size, void *stream);
 
 /*
+ * int4 weights in a load-time packed layout for the matrix-core GEMV.
+ *
+ * Operation: the offline weight repack with a versioned layout flag that the
+ * onnx-genai pull request #1000 proposes ("Roadmap recommendation"), for the
+ * MatMulNBits int4 weights of qgemv_int4_blockwise.  The packed buffer holds
+ * the same codes, scales and zero points, bit for bit, in another order;
+ * qgemv_int4_packed on it computes the product qgemv_int4_blockwise defines
+ * (same tolerance; the summation order is that of the packed kernel).
+ *
+ * Layout QG_INT4_LAYOUT_TILE16_V1 (K a positive multiple of 128 and of the
+ * block size bs in {32, 64, 128, 256}; NBI = max(1, 128/bs)):
+ *   rows in tiles of 16 (T = ceil(N/16), the last tile padded with zero
+ *   rows), each row's weights in items of 128 (C = K/128); tile t's item c
+ *   is a record of RB bytes at byte offset (t*C + c)*RB, RB = 1184 (bs 32),
+ *   1104 (bs 64) or 1072 (bs 128, 256):
+ *   bytes [0, 1024)     16 bytes per lane l = 16g + n (n, g = 0..15, 0..3):
+ *                       4-byte word j (j = 0..3) at 16l + 4j is the original
+ *                       4-byte word of row 16t + n at byte 64c + 16j + 4g
+ *                       (weights k = 128c + 32j + 8g .. +7);
+ *   [1024, 1024+32NBI)  fp16 scales [16][NBI]: entry (n, b) is the scale of
+ *                       row 16t + n, block 128c/bs + b (bs = 256: block c/2);
+ *   next 16 bytes (32 when NBI = 4)  zero points: max(1, NBI/2) bytes per
+ *                       row n; bits 4b..4b+3 hold the zero point of the
+ *                       same block (8 when zero_points was NULL), other
+ *                       bits 0.
+ *   Padding rows hold zero codes, scales and zero points.
+ * A layout flag other than QG_INT4_LAYOUT_TILE16_V1 returns
+ * QG_ERR_UNSUPPORTED, so a buffer written by a later layout version cannot
+ * be read as this one.
+ */
+#define QG_INT4_LAYOUT_TILE16_V1 1
+
+/* Bytes of the packed form of an N x K matrix with block size block_size in
+ * `layout`; 0 when the layout, block size or shape is not provided (N < 0,
+ * K not a positive multiple of 128 and of block_size). */
+size_t int4_packed_bytes(int64_t N, int64_t K, int32_t block_size,
+                         int32_t layout);
+
+/*
+ * int4_repack -- write the packed form of (w, scales, zero_points), whose
+ * layout and meaning are those of qgemv_int4_blockwise, into `packed`.  Run
+ * once per weight, on `stream`.
+ * w : [N][K/2] bytes, 4-byte aligned.  scales : fp16 bits [N][K/bs],
+ * 2-byte aligned.  zero_points : [N][ceil((K/bs)/2)] bytes or NULL
+ * (zero point 8).  packed : packed_bytes >= int4_packed_bytes(N, K,
+ * block_size, layout) bytes, 16-byte aligned, not overlapping an input
+ * (QG_ERR_BAD_SHAPE when too small, QG_ERR_ALIAS on overlap).  N == 0
+ * enqueues nothing.
+ */
+qg_status int4_repack(const uint8_t *w, const uint16_t *scales,
+                      const uint8_t *zero_points, uint8_t *packed,
+                      size_t packed_bytes, int64_t N, int64_t K,
+                      int32_t block_size, int32_t layout, void *stream);
+
+/*
+ * qgemv_int4_packed -- y = x . dequant(W)^T with W in the packed layout
+ * written by int4_repack (the same N, K, block_size and layout).
+ * x, x_type, y, y_type, ldx, ldy, M, N : as in qgemv_int4_blockwise.
+ * packed, packed_bytes : the packed weights (16-byte aligned) and the size
+ *                        of that buffer (QG_ERR_BAD_SHAPE when below
+ *                        int4_packed_bytes).
+ * Rows of x beyond what one launch keeps in LDS are run as groups of rows,
+ * each reading the weights again; K above about 80000 (one row of x no
+ * longer fits) returns QG_ERR_UNSUPPORTED.
+ */
+qg_status qgemv_int4_packed(const void *x, int64_t ldx, int32_t x_type,
+                            const uint8_t *packed, size_t packed_bytes,
+                            int32_t layout, void *y, int64_t ldy,
+                            int32_t y_type, int64_t M, int64_t N, int64_t K,
+                            int32_t block_size, void *stream);
+
+/*
  * qgemv_q4k -- q4_K GEMV, scale/min decoded inside the kernel.
  *
  * Operation: "62 . r59 -- q4_K W_dsc plane + riders", sections 2.1 and 3.2.

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
                             "q4k_dsc_plane_bytes", "q4k_build_dsc_plane", "qg_status_string",
                             "qg_last_error", "qg_last_launch", "qg_path_count", "qg_path_name",
                             "qg_path_launches", "q4k_mmq_workspace_bytes", "q8_quantize_rows",
-                            "qgemm_q4k_mmq", "qgemm_q4k_mmq_noalloc"])
+                            "qgemm_q4k_mmq", "qgemm_q4k_mmq_noalloc", "int4_packed_bytes",
+                            "int4_repack", "qgemv_int4_packed"])
 
 
 def test_library_exports_exactly_the_header():
@@ -115,6 +116,63 @@ def test_int4_validation():
     assert L.qg_last_error().decode() == ""
     # a huge w is refused up front (kernels address with 32-bit offsets)
     assert _int4(L, N=1 << 20, K=1 << 13, ldx=1 << 13, ldy=1 << 20) == QG_ERR_UNSUPPORTED
+
+
+def test_int4_packed_bytes():
+    """Records of 16 rows x 128 weights: 1024 code bytes + 32 scale bytes per
+    block of the item + 16 (32 for 4 blocks) zero-point bytes."""
+    L = q.load_library()
+    V1 = q.INT4_LAYOUT_TILE16_V1
+    assert L.int4_packed_bytes(16, 128, 32, V1) == 1184
+    assert L.int4_packed_bytes(16, 128, 64, V1) == 1104
+    assert L.int4_packed_bytes(16, 128, 128, V1) == 1072
+    assert L.int4_packed_bytes(16, 256, 256, V1) == 2 * 1072
+    assert L.int4_packed_bytes(17, 256, 32, V1) == 2 * 2 * 1184   # 2 tiles x 2 items
+    assert L.int4_packed_bytes(0, 4096, 32, V1) == 0
+    assert L.int4_packed_bytes(151936, 4096, 32, V1) == 9496 * 32 * 1184
+    for args in ((16, 100, 32, V1), (16, 64, 32, V1), (16, 128, 256, V1), (16, 128, 16, V1),
+                 (16, 128, 32, 2), (16, 128, 32, 0), (-1, 128, 32, V1)):
+        assert L.int4_packed_bytes(*args) == 0, args
+
+
+def _repack(L, w=B, s=C, zp=D, out=E, nbytes=1 << 20, N=16, K=256, bs=32, layout=1):
+    return L.int4_repack(w, s, zp, out, nbytes, N, K, bs, layout, None)
+
+
+def _packed(L, x=A, ldx=256, xt=0, wp=B, nbytes=1 << 20, layout=1, y=E, ldy=16, yt=0, M=1, N=16,
+            K=256, bs=32):
+    return L.qgemv_int4_packed(x, ldx, xt, wp, nbytes, layout, y, ldy, yt, M, N, K, bs, None)
+
+
+def test_int4_repack_and_packed_validation():
+    L = q.load_library()
+    assert _repack(L, w=None) == QG_ERR_NULL_POINTER
+    assert _repack(L, out=None) == QG_ERR_NULL_POINTER
+    assert _repack(L, layout=2) == QG_ERR_UNSUPPORTED
+    assert "layout" in L.qg_last_error().decode()
+    assert _repack(L, bs=16) == QG_ERR_UNSUPPORTED
+    assert _repack(L, K=96) == QG_ERR_BAD_SHAPE
+    assert _repack(L, K=128, bs=256) == QG_ERR_BAD_SHAPE
+    assert _repack(L, nbytes=2 * 1184 - 1) == QG_ERR_BAD_SHAPE
+    assert _repack(L, w=B + 2) == QG_ERR_MISALIGNED
+    assert _repack(L, out=E + 8) == QG_ERR_MISALIGNED
+    assert _repack(L, out=B + 64) == QG_ERR_ALIAS
+    assert _repack(L, N=0) == QG_OK
+    assert _packed(L, x=None) == QG_ERR_NULL_POINTER
+    assert _packed(L, wp=None) == QG_ERR_NULL_POINTER
+    assert _packed(L, layout=0) == QG_ERR_UNSUPPORTED
+    assert _packed(L, xt=1) == QG_ERR_UNSUPPORTED
+    assert _packed(L, M=9) == QG_ERR_BAD_SHAPE
+    assert _packed(L, K=192, ldx=192) == QG_ERR_BAD_SHAPE
+    assert _packed(L, nbytes=100) == QG_ERR_BAD_SHAPE
+    assert _packed(L, ldx=128) == QG_ERR_BAD_SHAPE
+    assert _packed(L, ldy=8) == QG_ERR_BAD_SHAPE
+    assert _packed(L, yt=5) == QG_ERR_UNSUPPORTED
+    assert _packed(L, wp=B + 8) == QG_ERR_MISALIGNED
+    assert _packed(L, y=E + 2, yt=2) == QG_ERR_MISALIGNED
+    assert _packed(L, y=B + 64) == QG_ERR_ALIAS
+    assert _packed(L, K=1 << 17, ldx=1 << 17, nbytes=1 << 24) == QG_ERR_UNSUPPORTED  # x beyond LDS
+    assert _packed(L, N=0) == QG_OK
 
 
 def _q4k(L, x=A, ldx=256, w=B, y=E, ldy=16, M=1, N=16, K=256, dsc=None, use_dsc=False):
@@ -257,7 +315,7 @@ def test_product_package_does_not_import_the_oracle():
 def test_liveness_exports_on_the_host():
     # host-only functions: no GPU needed
     names = q.path_names()
-    assert len(names) == q.load_library().qg_path_count() == 17
+    assert len(names) == q.load_library().qg_path_count() == 19
     assert names[0] == "int4_dot2_persistent" and "q4k_persistent_plane" in names
     assert q.load_library().qg_path_name(-1) is None
     assert q.load_library().qg_path_name(len(names)) is None

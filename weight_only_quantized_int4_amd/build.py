@@ -22,7 +22,8 @@ LIB = os.path.join(PKG, "libqgemv.so")
 PROBE_LIB = os.path.join(PKG, "libqgemv_readprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["qgemv_api.cpp", "int4_gemv.hip", "q4k_gemv.hip", "bf16_gemv.hip", "q4k_mmq.hip"]
+SOURCES = ["qgemv_api.cpp", "int4_gemv.hip", "int4_packed.hip", "q4k_gemv.hip", "bf16_gemv.hip",
+           "q4k_mmq.hip"]
 PROBE_SOURCES = ["read_probe.hip"]
 
 # -packed-fp32-ops: never emit v_pk_{add,mul,fma}_f32 (kept off on this target).

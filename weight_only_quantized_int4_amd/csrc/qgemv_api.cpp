@@ -31,7 +31,7 @@ const char* const kPathNames[qg::kPathCount] = {
     "int4_mfma_phased",     "q4k_persistent",       "q4k_persistent_plane", "q4k_tiled",
     "q4k_tiled_plane",      "q4k_plane_build",      "bf16_aligned",    "bf16_mfma_tiles",
     "bf16_mfma_split",      "bf16_general",         "q8_quantize",     "q4k_mmq",
-    "int4_span"};
+    "int4_span",            "int4_repack",          "int4_packed"};
 
 void begin_call() {
   g_last_launch[0] = '\0';
@@ -179,6 +179,88 @@ qg_status qgemv_int4_blockwise(const void* xv, int64_t ldx, int32_t x_type, cons
   return hip_status(qg::launch_int4_gemv(x, ldx, w, scales, zero_points, y, ldy, y_type, (int)M,
                                          (int)N, (int)K, block_size,
                                          static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t int4_packed_bytes(int64_t N, int64_t K, int32_t block_size, int32_t layout) {
+  if (layout != QG_INT4_LAYOUT_TILE16_V1 || N < 0 || K < 128 || K % 128 != 0 ||
+      (block_size != 32 && block_size != 64 && block_size != 128 && block_size != 256) ||
+      K % block_size != 0 || N > INT32_MAX || K > INT32_MAX)
+    return 0;
+  return (size_t)((N + 15) / 16) * (size_t)(K / 128) * (size_t)qg::int4_packed_record_bytes(block_size);
+}
+
+// Shape and layout checks shared by the repack and the packed GEMV.
+static qg_status packed_checks(const char* fn, int64_t N, int64_t K, int32_t block_size,
+                               int32_t layout, size_t packed_bytes, size_t* need) {
+  if (layout != QG_INT4_LAYOUT_TILE16_V1)
+    return fail(QG_ERR_UNSUPPORTED, "%s: layout %d (only QG_INT4_LAYOUT_TILE16_V1 = %d)", fn,
+                layout, QG_INT4_LAYOUT_TILE16_V1);
+  if (block_size != 32 && block_size != 64 && block_size != 128 && block_size != 256)
+    return fail(QG_ERR_UNSUPPORTED, "%s: block_size %d not in {32, 64, 128, 256}", fn, block_size);
+  if (N < 0 || N > INT32_MAX) return fail(QG_ERR_BAD_SHAPE, "%s: N = %lld", fn, (long long)N);
+  if (K < 128 || K > INT32_MAX || K % 128 != 0 || K % block_size != 0)
+    return fail(QG_ERR_BAD_SHAPE, "%s: K = %lld is not a positive multiple of 128 and of block_size %d",
+                fn, (long long)K, block_size);
+  *need = int4_packed_bytes(N, K, block_size, layout);
+  if (packed_bytes < *need)
+    return fail(QG_ERR_BAD_SHAPE, "%s: packed buffer of %zu bytes, the layout needs %zu", fn,
+                packed_bytes, *need);
+  return QG_OK;
+}
+
+qg_status int4_repack(const uint8_t* w, const uint16_t* scales, const uint8_t* zero_points,
+                      uint8_t* packed, size_t packed_bytes, int64_t N, int64_t K,
+                      int32_t block_size, int32_t layout, void* stream) {
+  begin_call();
+  static const char fn[] = "int4_repack";
+  if (!w || !scales || !packed) return fail(QG_ERR_NULL_POINTER, "%s: w, scales and packed are required", fn);
+  size_t need = 0;
+  if (qg_status s = packed_checks(fn, N, K, block_size, layout, packed_bytes, &need)) return s;
+  if (!aligned(w, 4) || !aligned(scales, 2) || !aligned(packed, 16))
+    return fail(QG_ERR_MISALIGNED, "%s: w must be 4-, scales 2- and packed 16-byte aligned", fn);
+  const int64_t nb = K / block_size;
+  const int64_t zrow = (nb + 1) / 2;
+  const Range rp = range_of(packed, (int64_t)need);
+  if (N > 0 && (overlap(rp, range_of(w, N * (K / 2))) || overlap(rp, range_of(scales, N * nb * 2)) ||
+                (zero_points && overlap(rp, range_of(zero_points, N * zrow)))))
+    return fail(QG_ERR_ALIAS, "%s: packed overlaps an input", fn);
+  if (N == 0) return ok();
+  return hip_status(qg::launch_int4_repack(w, scales, zero_points, packed, (int)N, (int)K,
+                                           block_size, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+qg_status qgemv_int4_packed(const void* xv, int64_t ldx, int32_t x_type, const uint8_t* packed,
+                            size_t packed_bytes, int32_t layout, void* y, int64_t ldy,
+                            int32_t y_type, int64_t M, int64_t N, int64_t K, int32_t block_size,
+                            void* stream) {
+  begin_call();
+  static const char fn[] = "qgemv_int4_packed";
+  const uint16_t* x = static_cast<const uint16_t*>(xv);
+  if (!x || !packed || !y) return fail(QG_ERR_NULL_POINTER, "%s: x, packed and y are required", fn);
+  if (x_type != QG_F16)
+    return fail(QG_ERR_UNSUPPORTED, "%s: x_type %d (only QG_F16 activations are provided)", fn,
+                x_type);
+  if (qg_status s = check_mnk(fn, M, N, K)) return s;
+  size_t need = 0;
+  if (qg_status s = packed_checks(fn, N, K, block_size, layout, packed_bytes, &need)) return s;
+  if (qg::int4_packed_max_rows_of_x((int)K) < 1)
+    return fail(QG_ERR_UNSUPPORTED, "%s: K = %lld: one row of x does not fit in LDS", fn, (long long)K);
+  if (!valid_out_dtype(y_type)) return fail(QG_ERR_UNSUPPORTED, "%s: y_type %d", fn, y_type);
+  if (qg_status s = check_ld(fn, "ldx", ldx, K)) return s;
+  if (qg_status s = check_ld(fn, "ldy", ldy, N)) return s;
+  if (!aligned(packed, 16)) return fail(QG_ERR_MISALIGNED, "%s: packed must be 16-byte aligned", fn);
+  if (!aligned(x, 2)) return fail(QG_ERR_MISALIGNED, "%s: x must be 2-byte aligned", fn);
+  const int ysz = dtype_size(y_type);
+  if (!aligned(y, ysz)) return fail(QG_ERR_MISALIGNED, "%s: y must be %d-byte aligned", fn, ysz);
+  const Range ry = range_of(y, ((M - 1) * ldy + N) * ysz);
+  if (N > 0 && (overlap(ry, range_of(x, ((M - 1) * ldx + K) * 2)) ||
+                overlap(ry, range_of(packed, (int64_t)need))))
+    return fail(QG_ERR_ALIAS, "%s: y overlaps an input", fn);
+  if (N == 0) return ok();
+  return hip_status(qg::launch_int4_gemv_packed(x, ldx, packed, y, ldy, y_type, (int)M, (int)N,
+                                                (int)K, block_size, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

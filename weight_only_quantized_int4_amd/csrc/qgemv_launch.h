@@ -30,6 +30,8 @@ enum Path : int {
   kPathQ8Quantize,
   kPathQ4kMmq,
   kPathInt4Span,
+  kPathInt4Repack,
+  kPathInt4Packed,
     kPathCount
 };
 
@@ -42,6 +44,17 @@ hipError_t launch_int4_gemv(const uint16_t* x, int64_t ldx, const uint8_t* w,
                             const uint16_t* scales, const uint8_t* zp, void* y,
                             int64_t ldy, int y_type, int M, int N, int K,
                             int block_size, hipStream_t stream);
+
+// int4 packed layout (int4_packed.hip): bytes of one record (16 rows x 128
+// weights with their scales and zero points), the rows of x one launch of the
+// packed GEMV holds in LDS for rows of K, the load-time repack, and the GEMV.
+int64_t int4_packed_record_bytes(int block_size);
+size_t int4_packed_max_rows_of_x(int K);
+hipError_t launch_int4_repack(const uint8_t* w, const uint16_t* scales, const uint8_t* zp,
+                              uint8_t* out, int N, int K, int block_size, hipStream_t stream);
+hipError_t launch_int4_gemv_packed(const uint16_t* x, int64_t ldx, const uint8_t* wp, void* y,
+                                   int64_t ldy, int y_type, int M, int N, int K, int block_size,
+                                   hipStream_t stream);
 
 hipError_t launch_q4k_gemv(const float* x, int64_t ldx, const uint8_t* w,
                            const float* dsc, float* y, int64_t ldy, int M, int N,

@@ -28,6 +28,8 @@ _X_TYPES = {torch.float16: QG_F16, torch.bfloat16: QG_BF16}
 # Size of the static device workspace of qgemm_q4k_mmq_noalloc
 # (QG_MMQ_NOALLOC_SCRATCH_BYTES in include/qgemv.h).
 MMQ_NOALLOC_SCRATCH_BYTES = 32 << 20
+# Layout flag of the packed int4 weights (QG_INT4_LAYOUT_TILE16_V1).
+INT4_LAYOUT_TILE16_V1 = 1
 
 
 class QgemvError(RuntimeError):
@@ -74,6 +76,10 @@ def load_library() -> ctypes.CDLL:
         "q8_quantize_rows": (St, [P, I64, P, P, I64, I64, P]),
         "qgemm_q4k_mmq": (St, [P, I64, P, P, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]),
         "qgemm_q4k_mmq_noalloc": (St, [P, I64, P, P, P, I64, I64, I64, I64, P]),
+        "int4_packed_bytes": (ctypes.c_size_t, [I64, I64, I32, I32]),
+        "int4_repack": (St, [P, P, P, P, ctypes.c_size_t, I64, I64, I32, I32, P]),
+        "qgemv_int4_packed": (St, [P, I64, I32, P, ctypes.c_size_t, I32, P, I64, I32, I64, I64,
+                                   I64, I32, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -174,6 +180,53 @@ def qgemv_int4_blockwise(x: torch.Tensor, w: torch.Tensor, scales: torch.Tensor,
         _dense(zero_points, "zero_points", (N, (nb + 1) // 2))
     _check("qgemv_int4_blockwise", load_library().qgemv_int4_blockwise(
         _ptr(x), _ld(x), _X_TYPES[x.dtype], _ptr(w), _ptr(scales), _ptr(zero_points), _ptr(y), _ld(y),
+        _OUT_TYPES[y.dtype], M, N, K, block_size, _stream(stream)))
+    return y
+
+
+def int4_packed_bytes(N: int, K: int, block_size: int, layout: int = INT4_LAYOUT_TILE16_V1) -> int:
+    """Bytes of the packed form (0 when the layout or shape is not provided)."""
+    return int(load_library().int4_packed_bytes(N, K, block_size, layout))
+
+
+def int4_repack(w: torch.Tensor, scales: torch.Tensor, zero_points: Optional[torch.Tensor],
+                packed: torch.Tensor, block_size: int, layout: int = INT4_LAYOUT_TILE16_V1,
+                stream=None) -> torch.Tensor:
+    """Write the packed layout of (w, scales, zero_points) -- as taken by
+    qgemv_int4_blockwise -- into ``packed`` (uint8, int4_packed_bytes bytes)."""
+    for t, n, d in ((w, "w", _U8), (scales, "scales", _F16), (zero_points, "zero_points", _U8),
+                    (packed, "packed", _U8)):
+        _arg(t, n, d)
+    if w.dim() != 2:
+        raise ValueError(f"w: expected a 2-D tensor [N, K/2], got shape {tuple(w.shape)}")
+    N, K = w.shape[0], 2 * w.shape[1]
+    _dense(w, "w", (N, K // 2))
+    if block_size > 0 and K % block_size == 0:  # otherwise the library rejects the call
+        nb = K // block_size
+        _dense(scales, "scales", (N, nb))
+        _dense(zero_points, "zero_points", (N, (nb + 1) // 2))
+    if not packed.is_contiguous():
+        raise ValueError("packed must be contiguous")
+    _check("int4_repack", load_library().int4_repack(
+        _ptr(w), _ptr(scales), _ptr(zero_points), _ptr(packed), packed.numel(), N, K, block_size,
+        layout, _stream(stream)))
+    return packed
+
+
+def qgemv_int4_packed(x: torch.Tensor, packed: torch.Tensor, y: torch.Tensor, block_size: int,
+                      layout: int = INT4_LAYOUT_TILE16_V1, stream=None) -> torch.Tensor:
+    """y[M,N] = x[M,K] . dequant(W)^T with W packed by int4_repack (N from y,
+    K from x).  x fp16 [M,K]; y fp16/bf16/fp32 [M,N]."""
+    for t, n, d in ((x, "x", tuple(_X_TYPES)), (packed, "packed", _U8), (y, "y", _OUT)):
+        _arg(t, n, d)
+    if y.dim() != 2:
+        raise ValueError(f"y: expected a 2-D tensor [M, N], got shape {tuple(y.shape)}")
+    N = y.shape[1]
+    M, K = _xy(x, y, N)
+    if not packed.is_contiguous():
+        raise ValueError("packed must be contiguous")
+    _check("qgemv_int4_packed", load_library().qgemv_int4_packed(
+        _ptr(x), _ld(x), _X_TYPES[x.dtype], _ptr(packed), packed.numel(), layout, _ptr(y), _ld(y),
         _OUT_TYPES[y.dtype], M, N, K, block_size, _stream(stream)))
     return y
 
