@@ -420,6 +420,8 @@ enum SpanPipe : int {
   kSpanDouble = 1,  // two register sets: the next span loads while one computes
   kSpanRing = 2,    // one register set: each piece is reloaded with the next
                     // span's piece as soon as it has been consumed
+  kSpanRing2 = 3,   // two register sets used in turn, each piece reloaded with
+                    // the piece of the span after next
 };
 
 template <int M, int R, int U, bool ZP, int PIPE>
@@ -568,6 +570,37 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_span(
       });
     }
     if (s < nspans) compute(bufA, s, nothing);
+  } else if constexpr (PIPE == kSpanRing2) {
+    // bufA holds span s, bufB span s + GW; every consumed piece is reloaded
+    // with the same piece of the span two steps on (unconditionally while
+    // three more spans follow, then under a wave-uniform bound).
+    if (gw + GW < nspans) load(bufB, gw + GW);
+    int s = gw;
+#pragma unroll 1
+    for (; s + 3 * GW < nspans; s += 2 * GW) {
+      compute(bufA, s, [&](int u) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) load_piece(bufA, s + 2 * GW, i, u);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      compute(bufB, s + GW, [&](int u) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) load_piece(bufB, s + 3 * GW, i, u);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    if (s < nspans) {
+      const bool third = s + 2 * GW < nspans;
+      compute(bufA, s, [&](int u) {
+        if (third) {
+#pragma unroll
+          for (int i = 0; i < R; ++i) load_piece(bufA, s + 2 * GW, i, u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if (s + GW < nspans) compute(bufB, s + GW, nothing);
+      if (third) compute(bufA, s + 2 * GW, nothing);
+    }
   } else {
 #pragma unroll 1
     for (int s = gw; s < nspans; s += GW) {

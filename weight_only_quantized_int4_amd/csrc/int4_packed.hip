@@ -289,7 +289,11 @@ hipError_t launch_repack_nbi(const uint8_t* w, const uint16_t* scales, const uin
 }
 
 // Waves per workgroup: 8, or fewer when a row has fewer than 8 items (every
-// wavefront must get at least one item of each tile).
+// wavefront must get at least one item of each tile); 16 when the matrix has
+// fewer tiles than the GPU has CUs, so that each tile's CU keeps more of its
+// bytes in flight.
+constexpr bool kPackedWide = true;
+constexpr int kPackedWideTiles = 256;
 template <int M, int NBI, int NW>
 hipError_t launch_packed_nw(const uint16_t* x, int64_t ldx, const uint8_t* wp, void* y,
                             int64_t ldy, int y_type, int N, int K, size_t shmem,
@@ -312,6 +316,11 @@ hipError_t launch_packed_m(const uint16_t* x, int64_t ldx, const uint8_t* wp, vo
                            int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
   const int C = K / 128;
   const size_t xbytes = (size_t)M * K * 2;
+  const int ntiles = (N + 15) / 16;
+  if (kPackedWide && C >= 16 && ntiles < kPackedWideTiles &&
+      xbytes + 16 * kWave * 16 <= (size_t)kLdsMax)
+    return launch_packed_nw<M, NBI, 16>(x, ldx, wp, y, ldy, y_type, N, K,
+                                        xbytes + 16 * kWave * 16, stream);
   if (C >= 8)
     return launch_packed_nw<M, NBI, 8>(x, ldx, wp, y, ldy, y_type, N, K,
                                        xbytes + 8 * kWave * 16, stream);

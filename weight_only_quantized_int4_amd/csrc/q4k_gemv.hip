@@ -276,7 +276,7 @@ __attribute__((amdgpu_waves_per_eu(M == 1 && NT == 1024 && D <= 2 ? 8 : 1)))
 void q4k_gemv_persistent(
     const float* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const float2* __restrict__ dsc, float* __restrict__ y, int64_t ldy, int N, int K,
-    int x_vec16) {
+    int x_vec16, int rows_q, int rows_r) {
   static_assert(!PL || (DSC && !STRIDED), "the plane tile needs the plane and contiguous rows");
   constexpr int NW = NT / kWave;  // wavefronts (rows in flight) per workgroup
   extern __shared__ float smem[];
@@ -291,8 +291,11 @@ void q4k_gemv_persistent(
   // wavefronts of the grid), so the resident wavefronts sweep one compact
   // window; otherwise a workgroup takes a contiguous range of rows.
   const int b = STRIDED ? (int)blockIdx.x : xcd_tile(blockIdx.x, gridDim.x);
-  const int r_begin = STRIDED ? 0 : (int)((int64_t)b * N / gridDim.x);
-  const int r_end = STRIDED ? N : (int)((int64_t)(b + 1) * N / gridDim.x);
+  // Contiguous ranges: the first rows_r workgroups take rows_q + 1 rows, the
+  // others rows_q (rows_q, rows_r = N / grid, N % grid from the host), so no
+  // wavefront divides.
+  const int r_begin = STRIDED ? 0 : b * rows_q + (b < rows_r ? b : rows_r);
+  const int r_end = STRIDED ? N : r_begin + rows_q + (b < rows_r ? 1 : 0);
   const int first = STRIDED ? b * NW + wv : r_begin + wv;
   const int rstep = STRIDED ? (int)gridDim.x * NW : NW;
   const int nsb = K >> 8;
@@ -392,11 +395,11 @@ void q4k_gemv_persistent(
     stage_slots<2>(
         tid, NT, M * v4,
         [&](int t) {
-          const int m = t / v4;
+          const int m = M == 1 ? 0 : t / v4;  // count = M * v4: one row needs no division
           return *reinterpret_cast<const uint4*>(x + m * ldx + 4 * (t - m * v4));
         },
         [&](int t, uint4 u) {
-          const int m = t / v4, i = t - m * v4;
+          const int m = M == 1 ? 0 : t / v4, i = t - m * v4;
           const int e = 4 * i;
           *reinterpret_cast<uint4*>(xs + m * XSTR + (e >> 6) * 68 + (e & 63)) = u;
         },
@@ -545,7 +548,7 @@ hipError_t launch_persistent(const float* x, int64_t ldx, const uint8_t* w, cons
         const int g2 = want < cap_pl ? want : cap_pl;
         if (g2 >= g) {  // the tile fits this grid: launch
           hipLaunchKernelGGL(kern_pl, dim3(g), dim3(NT), lds, stream, x, ldx, w, dsc2, y, ldy, N,
-                             K, x_vec16);
+                             K, x_vec16, N / g, N % g);
           note_launch(kPathQ4kPersistentPlane, M, g, NT, lds);
           return hipGetLastError();
         }
@@ -554,7 +557,7 @@ hipError_t launch_persistent(const float* x, int64_t ldx, const uint8_t* w, cons
     }
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), full, stream, x, ldx, w, dsc2, y, ldy, N, K,
-                     x_vec16);
+                     x_vec16, N / grid, N % grid);
   note_launch(dsc2 ? kPathQ4kPersistentPlane : kPathQ4kPersistent, M, grid, NT, full);
   return hipGetLastError();
 }
