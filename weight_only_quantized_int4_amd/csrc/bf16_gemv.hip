@@ -23,7 +23,7 @@
 namespace qg {
 namespace {
 
-template <int M, int LPR, int R>
+template <int M, int LPR, int R, int DG>
 __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw,
     void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int KC) {
@@ -57,7 +57,10 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
 #pragma unroll
       for (int i = 0; i < R; ++i) v[i] = load_stream16(w + (wo[i] + (uint32_t)(kc + 8 * p)));
     };
-    uint4 cur[R];
+    // A ring of DG pieces per lane: piece p + DG*LPR reloads the slot of
+    // piece p as soon as p is consumed, so DG 16-byte loads per row stay in
+    // flight.
+    uint4 ring[DG][R];
     __syncthreads();
     stage_slots<4>(
         tid, kBlock, M * P,
@@ -70,15 +73,12 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
           xs[m * G + (t - m * P)] = v;
         },
         [&] {
-          if (j < P) load(cur, j);
+#pragma unroll
+          for (int k = 0; k < DG; ++k)
+            if (j + k * LPR < P) load(ring[k], j + k * LPR);
         });
     __syncthreads();
-#pragma unroll 1
-    for (int p = j; p < P; p += LPR) {
-      uint4 nxt[R];
-      const bool more = p + LPR < P;
-      if (more) load(nxt, p + LPR);
-      const uint4* wv = cur;
+    auto consume = [&](const uint4 (&wv)[R], int p) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const uint4 xv = xs[m * G + p];
@@ -92,9 +92,16 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_aligned(
           acc[i][m] = t;
         }
       }
-      if (more) {
+    };
+#pragma unroll 1
+    for (int p = j; p < P; p += DG * LPR) {
 #pragma unroll
-        for (int i = 0; i < R; ++i) cur[i] = nxt[i];
+      for (int k = 0; k < DG; ++k) {
+        const int pk = p + k * LPR;
+        if (pk < P) {
+          consume(ring[k], pk);
+          if (pk + DG * LPR < P) load(ring[k], pk + DG * LPR);
+        }
       }
     }
   }
@@ -456,6 +463,13 @@ hipError_t launch_mfma(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_
                                                           xbytes, stream);
 }
 
+// 16-byte weight loads in flight per lane and row in the aligned kernel.
+constexpr int kAlignedDepth = 4;
+// Wavefronts per SIMD the v_dot2 kernels' rows should occupy (lanes per row
+// are widened up to that).
+constexpr int kBf16FillWaves = 8;
+constexpr int kBf16LongRowK = 4096;
+
 template <int M, int LPR, int R>
 hipError_t launch_aligned(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
                           int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
@@ -464,7 +478,7 @@ hipError_t launch_aligned(const uint16_t* x, int64_t ldx, const uint16_t* w, int
   int KC = (kLdsXBudget / (2 * M)) & ~7;
   if (KC > K) KC = K;
   const size_t shmem = (size_t)M * KC * 2;
-  hipLaunchKernelGGL((bf16_gemv_aligned<M, LPR, R>), dim3(grid), dim3(kBlock), shmem, stream, x,
+  hipLaunchKernelGGL((bf16_gemv_aligned<M, LPR, R, kAlignedDepth>), dim3(grid), dim3(kBlock), shmem, stream, x,
                      ldx, w, ldw, y, ldy, y_type, N, K, KC);
   note_launch(kPathBf16Aligned, M, grid, kBlock, shmem);
   return hipGetLastError();
@@ -499,7 +513,14 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t l
       return launch_mfma<M>(x, ldx, w, ldw, y, ldy, y_type, N, K, stream);
   }
   // 16 lanes per row, widened for short matrices (see widen_lanes_per_row).
-  const int lpr = widen_lanes_per_row(16, N, (K + 7) / 8);
+  // Rows of at least kBf16LongRowK weights are widened until they occupy
+  // kBf16FillWaves wavefronts per SIMD: a 16-byte piece holds 8 bf16 weights
+  // (32 int4 ones), so HBM needs more of them in flight.  Shorter rows keep
+  // the int4 kernels' target: wider rows there leave each lane about one
+  // piece, and each workgroup stages x for one or two rows (measured: 1536²
+  // 3.6 -> 4.3 us, 6912 x 1536 6.2 -> 7.8 us when widened).
+  const int64_t fill = K >= kBf16LongRowK ? kLanesToFill * kBf16FillWaves / 2 : kLanesToFill;
+  const int lpr = widen_lanes_per_row(16, N, (K + 7) / 8, fill);
   constexpr int R = (M <= 4) ? 2 : 1;
   if (aligned) {
     switch (lpr) {

@@ -441,9 +441,13 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_span(
   const int PS = (K >> 5) * 5;
   const uint32_t magic = vreg_const(0x64006400u);
   // Per-lane parts of the offsets (fixed for the whole kernel).
-  uint32_t lblk[U];
+  uint32_t lblk[U], zoff[U], woff[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) lblk[u] = ((uint32_t)(lane + kWave * u) << 5) >> bs_log2;
+  for (int u = 0; u < U; ++u) {
+    lblk[u] = ((uint32_t)(lane + kWave * u) << 5) >> bs_log2;
+    zoff[u] = lblk[u] >> 1;
+    woff[u] = (uint32_t)(lane + kWave * u) * 16u;
+  }
 
   struct Span {
     uint4 w[R][U];
@@ -454,12 +458,13 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_span(
   // row (their sums are not stored).
   auto load_piece = [&](Span& sp, int s, int i, int u) {
     const int row = s * R + i < N ? s * R + i : N - 1;  // wave-uniform
-    const uint8_t* wr = w + (size_t)row * (size_t)(K >> 1) + lane * 16;
+    // scalar row bases, 32-bit lane offsets: base + offset addressing
+    const uint8_t* wr = w + (size_t)row * (size_t)(K >> 1);
     const uint16_t* sr = scales + (size_t)row * (size_t)nb;
     const uint8_t* zr = zp + (size_t)row * (size_t)zrow;
-    sp.w[i][u] = load_stream16(wr + u * (kWave * 16));
+    sp.w[i][u] = load_stream16(wr + woff[u]);
     sp.s[i][u] = sr[lblk[u]];
-    sp.z[i][u] = ZP ? zr[lblk[u] >> 1] : 0x88u;
+    sp.z[i][u] = ZP ? zr[zoff[u]] : 0x88u;
   };
   auto load = [&](Span& sp, int s) {
 #pragma unroll
