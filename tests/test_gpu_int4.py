@@ -332,15 +332,21 @@ def test_layer_shapes_single_row_sampled(N, K, bs, asym):
     assert_accept(y[:, list(cols)], yr[:1], S[:1], "f32", f"int4 layer {N}x{K} bs={bs}")
 
 
-# Rows of 2048, 4096 or 8192 weights at M = 1 take the span kernel (4 KB runs
-# of 4, 2 or 1 whole rows per wavefront): ragged last spans (N not a multiple
-# of the rows per span, down to N = 1), every block size, both zero-point
+# Rows of P = K/32 pieces, 64(U-1) < P <= 64U with at most an eighth of the
+# last u's lanes idle, take the span kernel at M = 1 (runs of 4, 2 or 1 whole
+# rows per wavefront): ragged last spans (N not a multiple of the rows per
+# span, down to N = 1), rows that end inside a wavefront's last piece (K =
+# 8960, 11008, 13824), every U from 1 to 8, every block size, both zero-point
 # modes and every output type, on every column.
 @pytest.mark.parametrize("N,K,bs,asym,out_dtype", [
     (1, 2048, 32, True, torch.float32), (3, 4096, 64, False, torch.float16),
     (4099, 2048, 32, True, torch.bfloat16), (1001, 4096, 256, True, torch.float32),
     (517, 8192, 128, False, torch.float16), (2, 8192, 32, True, torch.float32),
-    (9000, 4096, 32, True, torch.float16)])
+    (9000, 4096, 32, True, torch.float16), (301, 6144, 64, True, torch.float32),
+    (77, 8960, 128, True, torch.float32), (130, 10240, 256, False, torch.bfloat16),
+    (513, 11008, 128, True, torch.float16), (5, 11008, 64, False, torch.float32),
+    (260, 13824, 32, True, torch.float32), (97, 14336, 128, True, torch.float16),
+    (33, 16384, 32, False, torch.float32)])
 def test_span_kernel_every_column(N, K, bs, asym, out_dtype):
     say(f"int4 span N={N} K={K} bs={bs} asym={asym} out={out_dtype}")
     p = int4_case(N, K, bs, asym, 900 + N % 97)
@@ -364,7 +370,7 @@ def test_span_kernel_strided_unaligned_x_and_strided_y():
     assert_accept(y, yr[:1], S[:1], "f16", "int4 span strided")
 
 
-@pytest.mark.parametrize("K", [2048, 4096, 8192])
+@pytest.mark.parametrize("K", [2048, 4096, 8192, 11008, 14336])
 def test_span_kernel_one_hot_is_bit_exact(K):
     """x = e_k through the span kernel, fp32 out: y[n] equals the oracle's
     dequantized w[n,k] bitwise, for k at the edges of each lane's pieces."""

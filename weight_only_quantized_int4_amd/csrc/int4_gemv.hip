@@ -399,21 +399,22 @@ __device__ __forceinline__ int span_value(int r) {
   else return ((r & 1) << 1) | (r >> 1);
 }
 
-// Span variant for rows of 64*U pieces (U = 1, 2, 4: K = 2048, 4096, 8192):
-// the matrix is cut into spans of R = 4/U consecutive rows, i.e. 4 KB of
-// contiguous weight bytes, and each wavefront streams whole spans (gw,
-// gw + GW, ... for global wavefront gw of GW).  Lane l takes pieces l + 64u
-// (u < U) of each of the span's rows, so each of the 4 weight loads a lane
-// issues per span is one contiguous 1 KB wavefront access and the 4 together
-// cover the span: every wavefront keeps 4 KB runs of HBM in flight
-// (measured: such runs stream about 9% faster than the same bytes read with
-// a grid-wide stride).  The span index is wave-uniform, so row offsets are
-// scalar and each load is a scalar base plus a fixed per-lane offset.  With
-// DB the next span is loaded while the current one is computed (two register
-// sets used in turn); otherwise occupancy hides the latency.  A span's R row
-// sums are reduced together across the wavefront and stored by one lane each.
-// Unpack, zero point, scale and MAC are those of the kernels above; x stays
-// in registers for the whole kernel (each lane always reads the same pieces).
+// Span variant, M = 1, for rows of P = K/32 pieces of 32 weights.  Lane l
+// takes pieces l + 64u (u < U) of a row, so each weight load of a lane is one
+// contiguous 1 KB wavefront access.  Rows of exactly 64U pieces (K = 2048,
+// 4096, 8192: U = 1, 2, 4) are cut into spans of R = 4/U consecutive rows,
+// i.e. 4 KB of contiguous weight bytes.  RAGGED rows, 64(U-1) < P < 64U
+// (U = 3..8), make spans of one row: in the last u the lanes past the row's
+// end read its last piece and add it with scale 0.  Each wavefront streams
+// whole spans (gw, gw + GW, ... for global wavefront gw of GW), which keeps
+// runs of about 4 KB of HBM in flight per wavefront (measured: such runs
+// stream about 9% faster than the same bytes read with a grid-wide stride).
+// The span index is wave-uniform, so row offsets are scalar and each load is
+// a scalar base plus a fixed per-lane offset.  PIPE picks how loads overlap
+// the compute (below).  A span's R row sums are reduced together across the
+// wavefront and stored by one lane each.  Unpack, zero point, scale and MAC
+// are those of the kernels above; x is staged once per workgroup in LDS and
+// each lane reads the same x slots for every span.
 // How a span kernel keeps loads in flight while it computes.
 enum SpanPipe : int {
   kSpanSerial = 0,  // load a span, then compute it (occupancy hides latency)
@@ -424,7 +425,7 @@ enum SpanPipe : int {
                     // the piece of the span after next
 };
 
-template <int M, int R, int U, bool ZP, int PIPE>
+template <int M, int R, int U, bool ZP, int PIPE, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void int4_gemv_span(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zp, int zrow,
@@ -441,12 +442,17 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_span(
   const int PS = (K >> 5) * 5;
   const uint32_t magic = vreg_const(0x64006400u);
   // Per-lane parts of the offsets (fixed for the whole kernel).
+  // Rows of P = K/32 pieces with 64(U-1) < P <= 64U: in the last u, lanes
+  // past the row's end read its last piece and add it with scale 0.
+  const int P = K >> 5;
+  int pc[U];
   uint32_t lblk[U], zoff[U], woff[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    lblk[u] = ((uint32_t)(lane + kWave * u) << 5) >> bs_log2;
+    pc[u] = !RAGGED || lane + kWave * u < P ? lane + kWave * u : P - 1;
+    lblk[u] = ((uint32_t)pc[u] << 5) >> bs_log2;
     zoff[u] = lblk[u] >> 1;
-    woff[u] = (uint32_t)(lane + kWave * u) * 16u;
+    woff[u] = (uint32_t)pc[u] * 16u;
   }
 
   struct Span {
@@ -497,13 +503,14 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_span(
     for (int k = 0; k < R * M; ++k) acc[k] = 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int p = lane + kWave * u;
+      const int p = pc[u];
+      const bool live = !RAGGED || u < U - 1 || lane + kWave * u < P;
       const int zsh = (int)(lblk[u] & 1) << 2;
       float sc[R];
       uint32_t blo[R], bhi[R];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        sc[i] = f16_to_f32(cur.s[i][u]);
+        sc[i] = live ? f16_to_f32(cur.s[i][u]) : 0.f;
         const uint32_t z = (cur.z[i][u] >> zsh) & 15u;
         blo[i] = 0xE400E400u + z * 0x00010001u;  // -(1024 + zp) in both halves
         bhi[i] = 0xD400D400u + z * 0x00100010u;  // -(64 + zp) in both halves
@@ -976,7 +983,7 @@ constexpr int kSpanRows = 4;
 
 // Span kernel launch: one resident round of workgroups (or fewer when the
 // spans run out first).
-template <int M, int R, int U>
+template <int M, int R, int U, bool RAGGED>
 hipError_t launch_span(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* scales,
                        const uint8_t* zp, void* y, int64_t ldy, int y_type, int N, int K,
                        int block_size, hipStream_t stream) {
@@ -985,7 +992,8 @@ hipError_t launch_span(const uint16_t* x, int64_t ldx, const uint8_t* w, const u
   const int zrow = ((K / block_size) + 1) / 2;
   const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
   const int nspans = (N + R - 1) / R;
-  auto kern = zp ? int4_gemv_span<M, R, U, true, kSpanPipe> : int4_gemv_span<M, R, U, false, kSpanPipe>;
+  auto kern = zp ? int4_gemv_span<M, R, U, true, kSpanPipe, RAGGED>
+                 : int4_gemv_span<M, R, U, false, kSpanPipe, RAGGED>;
   const int cap = resident_workgroups(kern, kBlock, shmem);
   const int want = (nspans + kBlock / kWave - 1) / (kBlock / kWave);
   const int grid = want < cap ? want : cap;
@@ -1163,11 +1171,14 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
   }
   if constexpr (M <= kSpanMaxM) {
     if (K == 2048)
-      return launch_span<M, kSpanRows / 1, 1>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+      return launch_span<M, kSpanRows / 1, 1, false>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
+                                                      block_size, stream);
     if (K == 4096)
-      return launch_span<M, kSpanRows / 2, 2>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+      return launch_span<M, kSpanRows / 2, 2, false>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
+                                                      block_size, stream);
     if (K == 8192)
-      return launch_span<M, kSpanRows / 4, 4>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+      return launch_span<M, kSpanRows / 4, 4, false>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
+                                                      block_size, stream);
   }
   // Lanes per row (measured on the 151936 x 4096 lm_head shape): 32 is best at
   // small M, 8 at large M (more rows share each x read).  Take the first
@@ -1184,6 +1195,23 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
       break;
     }
   lpr = widen_lanes_per_row(lpr, N, P, 2 * kLanesToFill, true);
+  if constexpr (M <= kSpanMaxM) {
+    // Matrices too short for the persistent kernel (rows widened past one
+    // wavefront, which takes the tiled kernel): the span kernel with a row per
+    // wavefront, when at most an eighth of the last u's lanes idle.
+    const int U = (P + kWave - 1) / kWave;
+    if (lpr > kWave && U >= 3 && U <= 8 && (U * kWave - P) * 8 <= U * kWave &&
+        (size_t)M * P * 80 <= (size_t)kLdsBudget) {
+#define QG_SPAN(UU) \
+  case UU:          \
+    return launch_span<M, 1, UU, true>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
+      switch (U) {
+        QG_SPAN(3) QG_SPAN(4) QG_SPAN(5) QG_SPAN(6) QG_SPAN(7) QG_SPAN(8)
+        default: break;
+      }
+#undef QG_SPAN
+    }
+  }
 #define QG_LAUNCH(L, RR) \
   return launch_cfg<M, L, RR>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream)
   switch (lpr) {
