@@ -332,12 +332,13 @@ def test_layer_shapes_single_row_sampled(N, K, bs, asym):
     assert_accept(y[:, list(cols)], yr[:1], S[:1], "f32", f"int4 layer {N}x{K} bs={bs}")
 
 
-# Rows of P = K/32 pieces, 64(U-1) < P <= 64U with at most an eighth of the
-# last u's lanes idle, take the span kernel at M = 1 (runs of 4, 2 or 1 whole
-# rows per wavefront): ragged last spans (N not a multiple of the rows per
-# span, down to N = 1), rows that end inside a wavefront's last piece (K =
-# 8960, 11008, 13824), every U from 1 to 8, every block size, both zero-point
-# modes and every output type, on every column.
+# At M = 1, rows of 2048, 4096 or 8192 weights, and the rows of matrices too
+# short for the persistent kernel with P = K/32 pieces, 128 < P <= 512, take
+# the span kernel (runs of 4, 2 or 1 whole rows per wavefront): ragged last
+# spans (N not a multiple of the rows per span, down to N = 1), rows that end
+# inside a wavefront's last piece (K = 4864, 6912, 8960, 11008, 13824), every
+# U from 1 to 8, every block size, both zero-point modes and every output
+# type, on every column.
 @pytest.mark.parametrize("N,K,bs,asym,out_dtype", [
     (1, 2048, 32, True, torch.float32), (3, 4096, 64, False, torch.float16),
     (4099, 2048, 32, True, torch.bfloat16), (1001, 4096, 256, True, torch.float32),
@@ -346,7 +347,8 @@ def test_layer_shapes_single_row_sampled(N, K, bs, asym):
     (77, 8960, 128, True, torch.float32), (130, 10240, 256, False, torch.bfloat16),
     (513, 11008, 128, True, torch.float16), (5, 11008, 64, False, torch.float32),
     (260, 13824, 32, True, torch.float32), (97, 14336, 128, True, torch.float16),
-    (33, 16384, 32, False, torch.float32)])
+    (33, 16384, 32, False, torch.float32), (896, 4864, 32, True, torch.float16),
+    (1536, 6912, 128, False, torch.float32)])
 def test_span_kernel_every_column(N, K, bs, asym, out_dtype):
     say(f"int4 span N={N} K={K} bs={bs} asym={asym} out={out_dtype}")
     p = int4_case(N, K, bs, asym, 900 + N % 97)

@@ -1197,10 +1197,13 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
   lpr = widen_lanes_per_row(lpr, N, P, 2 * kLanesToFill, true);
   if constexpr (M <= kSpanMaxM) {
     // Matrices too short for the persistent kernel (rows widened past one
-    // wavefront, which takes the tiled kernel): the span kernel with a row per
-    // wavefront, when at most an eighth of the last u's lanes idle.
+    // wavefront, which takes the tiled kernel, so P >= 128 and, rows of
+    // exactly 128 pieces taking the span kernel above, U >= 3): the span
+    // kernel with a row per wavefront (measured faster than the tiled kernel
+    // also with up to 40 of the last u's 64 lanes idle: 896 x 4864, 1536 x
+    // 6912).
     const int U = (P + kWave - 1) / kWave;
-    if (lpr > kWave && U >= 3 && U <= 8 && (U * kWave - P) * 8 <= U * kWave &&
+    if (lpr > kWave && U >= 3 && U <= 8 &&
         (size_t)M * P * 80 <= (size_t)kLdsBudget) {
 #define QG_SPAN(UU) \
   case UU:          \
