@@ -153,17 +153,64 @@ def test_packed_strided_unaligned_x_and_strided_y(out_dtype):
     assert_accept(y, yr[:M], S[:M], OUT_NAME[out_dtype], "int4 packed strided")
 
 
+def _unaligned_x(p, M, K):
+    """x[:M] as a view whose rows start 2 bytes past a 16-byte boundary."""
+    buf = np.zeros(1 + M * K, dtype=np.uint16)
+    buf[1:] = p.x[:M].reshape(-1)
+    xt = f16_dev(buf)[1:].view(M, K)
+    assert xt.data_ptr() % 16 == 2
+    return xt
+
+
 def test_packed_rows_of_x_in_groups():
-    """K = 16384 at M = 8: x does not fit in LDS at once, so the rows run in
-    groups (each a launch)."""
+    """K = 16384 at M = 8 with x not 16-byte aligned: x is staged in LDS,
+    where it does not fit at once, so the rows run in groups (each a
+    launch)."""
     N, K, bs, M = 100, 16384, 128, 8
     say(f"int4 packed row groups N={N} K={K} M={M}")
     p = int4_case(N, K, bs, True, 71)
     packed = _pack(p, N, K, bs)
-    y = y_host(_run(packed, p, M, bs, torch.float32))
+    y = y_host(_run(packed, p, M, bs, torch.float32, x=_unaligned_x(p, M, K)))
     assert q.last_launch().count("int4_packed") >= 2, q.last_launch()
     yr, S = int4_ref(N, K, bs, True, 71)
     assert_accept(y, yr[:M], S[:M], "f32", "int4 packed row groups")
+
+
+@pytest.mark.parametrize("N,K,bs,M", [(100, 16384, 128, 8), (4100, 11008, 32, 8),
+                                      (300, 32768, 64, 5)])
+def test_packed_x_from_global_memory_any_row_length(N, K, bs, M):
+    """Aligned x whose rows LDS cannot hold reads the A operands from global
+    memory: one launch, no workgroup LDS for x."""
+    say(f"int4 packed x from global N={N} K={K} bs={bs} M={M}")
+    p = int4_case(N, K, bs, True, 72)
+    packed = _pack(p, N, K, bs)
+    y = y_host(_run(packed, p, M, bs, torch.float32))
+    launch = q.last_launch()
+    assert launch.count("int4_packed") == 1, launch
+    assert int(launch.split("lds=")[1].split()[0]) <= 16 * 1024, launch
+    yr, S = int4_ref(N, K, bs, True, 72)
+    assert_accept(y, yr[:M], S[:M], "f32", f"int4 packed x from global {N}x{K}")
+
+
+@pytest.mark.parametrize("N,K,bs", [(1536, 16384, 128), (37, 12288, 32)])
+def test_packed_x_staged_and_x_from_global_agree(N, K, bs):
+    """The same problem (M = 8 rows of x, more than LDS holds) with 16-byte
+    aligned x (A operands from global memory, one launch) and with unaligned
+    x (staged in LDS, groups of rows): both within the bound of the oracle,
+    and equal to each other bit for bit (the same MFMA chain per row)."""
+    M = 8
+    say(f"int4 packed staged vs global x N={N} K={K} bs={bs}")
+    p = int4_case(N, K, bs, True, 73)
+    packed = _pack(p, N, K, bs)
+    ya = _run(packed, p, M, bs, torch.float32)
+    la = q.last_launch()
+    yb = _run(packed, p, M, bs, torch.float32, x=_unaligned_x(p, M, K))
+    lb = q.last_launch()
+    assert la != lb, (la, lb)
+    yr, S = int4_ref(N, K, bs, True, 73)
+    assert_accept(y_host(ya), yr[:M], S[:M], "f32", "int4 packed x from global")
+    assert_accept(y_host(yb), yr[:M], S[:M], "f32", "int4 packed staged x")
+    assert torch.equal(ya.cpu().view(torch.int32), yb.cpu().view(torch.int32))
 
 
 def test_packed_is_deterministic():

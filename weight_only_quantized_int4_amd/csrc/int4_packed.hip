@@ -107,12 +107,20 @@ __global__ __launch_bounds__(kBlock) void int4_repack_kernel(
 // At a tile's end the wavefronts' partial sums meet in LDS and wavefront 0
 // adds them in wavefront order (deterministic) and stores the tile's 16
 // columns.
-template <int M, int NBI, int NW>
+// XG: x is not staged in LDS; each item's four A operands are loaded from
+// global memory (16 bytes per lane, 16-byte aligned rows of x) together with
+// the item's weights, into the same ring.  Used for rows of x that LDS cannot
+// hold at once, instead of one launch (and one pass over the weights) per
+// group of rows: 4096 x 11008 at M = 8 takes 13.3 us cold against 19.5 in
+// two groups.  Where x fits, staging it is faster (1536 x 6912, M = 8: 7.8
+// against 10.3 us; on the 151936-row lm_head more than twice as fast): each
+// workgroup reads x from L2 once instead of once per wavefront.
+template <int M, int NBI, int NW, bool XG>
 __global__ __launch_bounds__(NW * kWave) void int4_gemv_packed(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wp,
     void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int ntiles, int x_vec16) {
   using Geo = PackedGeom<NBI>;
-  constexpr int DG = 4;                                 // items in flight per lane
+  constexpr int DG = XG ? 2 : 4;                        // items in flight per lane
   constexpr int PPB = NBI == 4 ? 1 : NBI == 2 ? 2 : 4;  // MFMAs per scale block
   extern __shared__ uint4 xs[];  // [M][K/8] swizzled x slots, then [NW][64] partials
   const int tid = threadIdx.x;
@@ -133,6 +141,7 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_packed(
     uint4 w;
     SType s;
     uint32_t z;
+    uint4 a[4];  // XG: the item's x operands, as loaded
   };
   struct Cursor {
     int tile, c;
@@ -143,9 +152,17 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_packed(
       cu.tile += G;
     }
   };
+  // Rows of x for the A operand: rows >= M repeat real rows (their outputs
+  // are not stored).
+  const int arow = n < M ? n : n % M;
+  const uint16_t* xrow = x + (size_t)arow * (size_t)ldx + 8 * g;
   auto load = [&](Item& it, const Cursor& cu) {
     const uint8_t* rec = wp + ((size_t)cu.tile * (size_t)C + (size_t)cu.c) * Geo::kRecord;
     it.w = load_stream16(rec + 16 * lane);
+    if constexpr (XG) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) it.a[t] = load16(xrow + (cu.c * 128 + 32 * t));
+    }
     const uint8_t* sp = rec + 1024 + n * (2 * NBI);
     if constexpr (NBI == 4) it.s = *reinterpret_cast<const uint2*>(sp);
     else if constexpr (NBI == 2) it.s = *reinterpret_cast<const uint32_t*>(sp);
@@ -158,33 +175,37 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_packed(
   // XOR-swizzled on the bits that select the MFMA within an item.
   Item ring[DG];
   Cursor lc = {(int)blockIdx.x, i0};
-  stage_slots<4>(
-      tid, NW * kWave, M * S8,
-      [&](int t) {
-        const int m = t / S8;
-        return load_x8(x + m * ldx + (t - m * S8) * 8, x_vec16);
-      },
-      [&](int t, uint4 v) {
-        const int m = t / S8;
-        const int gi = t - m * S8;
-        xs[m * S8 + (gi ^ ((m & 3) << 2))] = pair_halves(v);
-      },
-      [&] {
+  auto fill_ring = [&] {
 #pragma unroll
-        for (int k = 0; k < DG; ++k) {
-          if (k < total) load(ring[k], lc);
-          advance(lc);
-        }
-      });
-  __syncthreads();
+    for (int k = 0; k < DG; ++k) {
+      if (k < total) load(ring[k], lc);
+      advance(lc);
+    }
+  };
+  if constexpr (XG) {
+    fill_ring();
+  } else {
+    stage_slots<4>(
+        tid, NW * kWave, M * S8,
+        [&](int t) {
+          const int m = t / S8;
+          return load_x8(x + m * ldx + (t - m * S8) * 8, x_vec16);
+        },
+        [&](int t, uint4 v) {
+          const int m = t / S8;
+          const int gi = t - m * S8;
+          xs[m * S8 + (gi ^ ((m & 3) << 2))] = pair_halves(v);
+        },
+        fill_ring);
+    __syncthreads();
+  }
 
-  const int arow = n < M ? n : n % M;
   uint32_t aoff[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
     aoff[t] = (uint32_t)((arow * S8 + ((4 * t + g) ^ ((arow & 3) << 2))) * 16);
   const char* xs_bytes = reinterpret_cast<const char*>(xs);
-  f32x4* red = reinterpret_cast<f32x4*>(xs + M * S8);  // [NW][64]
+  f32x4* red = reinterpret_cast<f32x4*>(xs + (XG ? 0 : M * S8));  // [NW][64]
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -194,7 +215,8 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_packed(
     uint4 av[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      av[t] = *reinterpret_cast<const uint4*>(xs_bytes + (aoff[t] + ibase));
+      av[t] = XG ? pair_halves(it.a[t])
+                 : *reinterpret_cast<const uint4*>(xs_bytes + (aoff[t] + ibase));
     f32x4 d = zero4;
     uint32_t bias_lo = 0, bias_hi = 0;
 #pragma unroll
@@ -226,7 +248,9 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_packed(
       __syncthreads();
       if (wave == 0) {
         f32x4 sum = red[lane];
-#pragma unroll
+        // (a partly unrolled loop: a full unroll would hold every
+        // wavefront's partials in registers at once)
+#pragma unroll 4
         for (int v = 1; v < NW; ++v) {
           const f32x4 o = red[v * kWave + lane];
 #pragma unroll
@@ -294,11 +318,15 @@ hipError_t launch_repack_nbi(const uint8_t* w, const uint16_t* scales, const uin
 // bytes in flight.
 constexpr bool kPackedWide = true;
 constexpr int kPackedWideTiles = 256;
-template <int M, int NBI, int NW>
+// When x is read from global memory (XG) instead of LDS: 0 never, 1 for rows
+// of x that LDS cannot hold, 2 always (x 16-byte aligned rows in every case).
+constexpr int kPackedXg = 1;
+
+template <int M, int NBI, int NW, bool XG>
 hipError_t launch_packed_nw(const uint16_t* x, int64_t ldx, const uint8_t* wp, void* y,
-                            int64_t ldy, int y_type, int N, int K, size_t shmem,
-                            hipStream_t stream) {
-  auto kern = int4_gemv_packed<M, NBI, NW>;
+                            int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
+  const size_t shmem = (XG ? 0 : (size_t)M * K * 2) + (size_t)NW * kWave * 16;
+  auto kern = int4_gemv_packed<M, NBI, NW, XG>;
   const hipError_t e = allow_lds(kern, shmem);
   if (e != hipSuccess) return e;
   const int ntiles = (N + 15) / 16;
@@ -311,36 +339,30 @@ hipError_t launch_packed_nw(const uint16_t* x, int64_t ldx, const uint8_t* wp, v
   return hipGetLastError();
 }
 
-template <int M, int NBI>
+template <int M, int NBI, bool XG>
 hipError_t launch_packed_m(const uint16_t* x, int64_t ldx, const uint8_t* wp, void* y,
                            int64_t ldy, int y_type, int N, int K, hipStream_t stream) {
   const int C = K / 128;
-  const size_t xbytes = (size_t)M * K * 2;
+  const size_t xbytes = XG ? 0 : (size_t)M * K * 2;
   const int ntiles = (N + 15) / 16;
   if (kPackedWide && C >= 16 && ntiles < kPackedWideTiles &&
       xbytes + 16 * kWave * 16 <= (size_t)kLdsMax)
-    return launch_packed_nw<M, NBI, 16>(x, ldx, wp, y, ldy, y_type, N, K,
-                                        xbytes + 16 * kWave * 16, stream);
-  if (C >= 8)
-    return launch_packed_nw<M, NBI, 8>(x, ldx, wp, y, ldy, y_type, N, K,
-                                       xbytes + 8 * kWave * 16, stream);
-  if (C >= 4)
-    return launch_packed_nw<M, NBI, 4>(x, ldx, wp, y, ldy, y_type, N, K,
-                                       xbytes + 4 * kWave * 16, stream);
-  if (C >= 2)
-    return launch_packed_nw<M, NBI, 2>(x, ldx, wp, y, ldy, y_type, N, K,
-                                       xbytes + 2 * kWave * 16, stream);
-  return launch_packed_nw<M, NBI, 1>(x, ldx, wp, y, ldy, y_type, N, K, xbytes + kWave * 16,
-                                     stream);
+    return launch_packed_nw<M, NBI, 16, XG>(x, ldx, wp, y, ldy, y_type, N, K, stream);
+  if (C >= 8) return launch_packed_nw<M, NBI, 8, XG>(x, ldx, wp, y, ldy, y_type, N, K, stream);
+  if (C >= 4) return launch_packed_nw<M, NBI, 4, XG>(x, ldx, wp, y, ldy, y_type, N, K, stream);
+  if (C >= 2) return launch_packed_nw<M, NBI, 2, XG>(x, ldx, wp, y, ldy, y_type, N, K, stream);
+  return launch_packed_nw<M, NBI, 1, XG>(x, ldx, wp, y, ldy, y_type, N, K, stream);
 }
 
 template <int NBI>
 hipError_t launch_packed_nbi(const uint16_t* x, int64_t ldx, const uint8_t* wp, void* y,
-                             int64_t ldy, int y_type, int M, int N, int K, hipStream_t stream) {
+                             int64_t ldy, int y_type, int M, int N, int K, bool xg,
+                             hipStream_t stream) {
   switch (M) {
 #define QG_CASE(MM) \
   case MM:          \
-    return launch_packed_m<MM, NBI>(x, ldx, wp, y, ldy, y_type, N, K, stream);
+    return xg ? launch_packed_m<MM, NBI, true>(x, ldx, wp, y, ldy, y_type, N, K, stream) \
+              : launch_packed_m<MM, NBI, false>(x, ldx, wp, y, ldy, y_type, N, K, stream);
     QG_CASE(1) QG_CASE(2) QG_CASE(3) QG_CASE(4) QG_CASE(5) QG_CASE(6) QG_CASE(7) QG_CASE(8)
 #undef QG_CASE
     default:
@@ -372,11 +394,13 @@ hipError_t launch_int4_repack(const uint8_t* w, const uint16_t* scales, const ui
 hipError_t launch_int4_gemv_packed(const uint16_t* x, int64_t ldx, const uint8_t* wp, void* y,
                                    int64_t ldy, int y_type, int M, int N, int K, int block_size,
                                    hipStream_t stream) {
-  // Rows of x beyond what LDS holds: groups of rows, each a launch that
-  // re-reads the weights.
+  // Rows of x beyond what LDS holds: x from global memory, or (x not 16-byte
+  // aligned) groups of rows, each a launch that re-reads the weights.
   const int mfit = (int)int4_packed_max_rows_of_x(K);
-  if (mfit < 1) return hipErrorInvalidValue;
-  if (M > mfit) {
+  const bool x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
+  const bool xg = x_vec16 && (kPackedXg == 2 || (kPackedXg == 1 && M > mfit));
+  if (!xg && mfit < 1) return hipErrorInvalidValue;
+  if (!xg && M > mfit) {
     for (int m0 = 0; m0 < M; m0 += mfit) {
       const int mm = M - m0 < mfit ? M - m0 : mfit;
       const size_t ysz = y_type == 2 ? 4 : 2;
@@ -387,9 +411,11 @@ hipError_t launch_int4_gemv_packed(const uint16_t* x, int64_t ldx, const uint8_t
     }
     return hipSuccess;
   }
-  if (block_size == 32) return launch_packed_nbi<4>(x, ldx, wp, y, ldy, y_type, M, N, K, stream);
-  if (block_size == 64) return launch_packed_nbi<2>(x, ldx, wp, y, ldy, y_type, M, N, K, stream);
-  return launch_packed_nbi<1>(x, ldx, wp, y, ldy, y_type, M, N, K, stream);
+  if (block_size == 32)
+    return launch_packed_nbi<4>(x, ldx, wp, y, ldy, y_type, M, N, K, xg, stream);
+  if (block_size == 64)
+    return launch_packed_nbi<2>(x, ldx, wp, y, ldy, y_type, M, N, K, xg, stream);
+  return launch_packed_nbi<1>(x, ldx, wp, y, ldy, y_type, M, N, K, xg, stream);
 }
 
 }  // namespace qg
