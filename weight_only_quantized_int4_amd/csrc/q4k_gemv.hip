@@ -102,8 +102,10 @@ __device__ __forceinline__ void piece_coeffs(const Q4kPiece& cur, int g, float& 
 // multiplies it back to dv*q inside the fused multiply-add, whose one
 // rounding is that of dv*q + mv.  A nibble in bits 4..7 is 16q * 2^-24 and
 // takes dv * 2^20.  So the unpack is one AND per pair of weights (no bias
-// to subtract).  The two chunks accumulate into separate registers (two
-// dependency chains).
+// to subtract).  For M < 4 the two chunks accumulate into separate registers
+// (two dependency chains per row of x); from M = 4 on, the M rows already
+// give enough independent chains and one register per row keeps the
+// 1024-thread kernels within 128 VGPRs (M = 8 spilled otherwise).
 template <int M, int NW>
 __device__ __forceinline__ void words_mac(const uint32_t (&words)[NW], const float* xa, int XSTR,
                                           float dva, float mva, float dvb, float mvb,
@@ -133,17 +135,26 @@ __device__ __forceinline__ void words_mac(const uint32_t (&words)[NW], const flo
     for (int m = 0; m < M; ++m) {
       const float4 xa4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 4 * t);
       const float4 xb4 = *reinterpret_cast<const float4*>(xa + m * XSTR + 32 + 4 * t);
-      float u = acc_a[m], v = acc_b[m];
+      float u = acc_a[m];
       u = __builtin_fmaf(wa0, xa4.x, u);
       u = __builtin_fmaf(wa1, xa4.y, u);
       u = __builtin_fmaf(wa2, xa4.z, u);
       u = __builtin_fmaf(wa3, xa4.w, u);
+      float v = M < 4 ? acc_b[m] : u;
       v = __builtin_fmaf(wb0, xb4.x, v);
       v = __builtin_fmaf(wb1, xb4.y, v);
       v = __builtin_fmaf(wb2, xb4.z, v);
       v = __builtin_fmaf(wb3, xb4.w, v);
-      acc_a[m] = u;
-      acc_b[m] = v;
+      if constexpr (M < 4) {
+        acc_a[m] = u;
+        acc_b[m] = v;
+      } else {
+        acc_a[m] = v;
+      }
+      // From M = 6 on, keep the x reads of the next four rows below the
+      // FMAs of these (hoisting all of them needs more than 128 VGPRs).
+      if constexpr (M >= 6)
+        if (m % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(NT) void q4k_gemv_kernel(
 
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const float v = group_sum<LPR>(acc_a[m] + acc_b[m]);
+    const float v = group_sum<LPR>(M < 4 ? acc_a[m] + acc_b[m] : acc_a[m]);
     if (j == 0 && n < N) y[m * ldy + n] = v;
   }
 }
@@ -444,7 +455,7 @@ void q4k_gemv_persistent(
     if (it == PPI - 1) {  // row finished (uniform across the wavefront)
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const float v = group_sum<kWave>(acc_a[m] + acc_b[m]);
+        const float v = group_sum<kWave>(M < 4 ? acc_a[m] + acc_b[m] : acc_a[m]);
         acc_a[m] = acc_b[m] = 0.f;
         if (j == 0) y[m * ldy + row] = v;
       }
