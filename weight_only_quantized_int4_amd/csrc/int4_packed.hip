@@ -248,13 +248,23 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_packed(
       __syncthreads();
       if (wave == 0) {
         f32x4 sum = red[lane];
-        // (a partly unrolled loop: a full unroll would hold every
-        // wavefront's partials in registers at once)
-#pragma unroll 4
-        for (int v = 1; v < NW; ++v) {
+        auto add_share = [&](int v) {
           const f32x4 o = red[v * kWave + lane];
 #pragma unroll
           for (int i = 0; i < 4; ++i) sum[i] += o[i];
+        };
+        // 16 wavefronts with x in LDS (small matrices, one workgroup per CU):
+        // a full unroll (measured faster, 1536 x 6912 at M = 8: 7.8 against
+        // 8.1 us).  Otherwise a partial one: holding every wavefront's
+        // partials at once raises the register count, so that fewer
+        // workgroups stay resident (the lm_head at M = 4: 72.4 against 68.5
+        // us) or, with x from global memory, registers spill.
+        if constexpr (NW >= 16 && !XG) {
+#pragma unroll
+          for (int v = 1; v < NW; ++v) add_share(v);
+        } else {
+#pragma unroll 4
+          for (int v = 1; v < NW; ++v) add_share(v);
         }
         const int col = cu.tile * 16 + n;
 #pragma unroll
