@@ -3,7 +3,10 @@
 Each source is compiled to an object under ``_build/`` (in parallel), then the
 objects are linked into ``weight_only_quantized_int4_amd/libqgemv.so``.  The
 bench's streaming-read probe (``read_probe.hip``) is linked into a library of
-its own, ``libqgemv_readprobe.so``, so the product library never holds it.
+its own, ``libqgemv_readprobe.so``, and ``libqgemv_wavetimes.so`` is the product
+library rebuilt with ``QG_WAVE_TIMES`` (the int4 span kernel records per-wave
+timestamps, read by ``bench.py --wave-times``), so the product library never
+holds either.
 hipcc cross-compiles for gfx950 without a GPU.
 """
 from __future__ import annotations
@@ -20,6 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqgemv.so")
 PROBE_LIB = os.path.join(PKG, "libqgemv_readprobe.so")
+WAVE_TIMES_LIB = os.path.join(PKG, "libqgemv_wavetimes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["qgemv_api.cpp", "int4_gemv.hip", "int4_packed.hip", "q4k_gemv.hip", "bf16_gemv.hip",
@@ -43,8 +47,8 @@ FLAGS = [
 SOURCE_FLAGS = {"q4k_mmq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
     cmd = [HIPCC, "-x", "hip", *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,17 +68,23 @@ def _link(objs, out: str) -> None:
 
 def build(extra_flags=(), out: str = LIB, verbose: bool = False, probe: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + (PROBE_SOURCES if probe else [])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra_flags)), srcs)))
-    _link([objs[s] for s in SOURCES], out)
+    jobs = [(s, "", list(extra_flags)) for s in SOURCES]
+    if probe:
+        jobs += [(s, "", list(extra_flags)) for s in PROBE_SOURCES]
+        jobs.append(("int4_gemv.hip", "_wt", list(extra_flags) + ["-DQG_WAVE_TIMES"]))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        done = list(ex.map(lambda j: _compile(j[0], j[2], j[1]), jobs))
+    objs = {(s, t): o for (s, t, _), o in zip(jobs, done)}
+    _link([objs[(s, "")] for s in SOURCES], out)
     _write_build_info(out)
     if verbose:
         print(f"built {out}")
     if probe:
-        _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
+        _link([objs[(s, "")] for s in PROBE_SOURCES], PROBE_LIB)
+        _link([objs[(s, "_wt" if s == "int4_gemv.hip" else "")] for s in SOURCES], WAVE_TIMES_LIB)
         if verbose:
             print(f"built {PROBE_LIB}")
+            print(f"built {WAVE_TIMES_LIB}")
     return out
 
 

@@ -415,6 +415,26 @@ __device__ __forceinline__ int span_value(int r) {
 // wavefront and stored by one lane each.  Unpack, zero point, scale and MAC
 // are those of the kernels above; x is staged once per workgroup in LDS and
 // each lane reads the same x slots for every span.
+#ifdef QG_WAVE_TIMES
+// Bench-only build (libqgemv_wavetimes.so, never the product library): the
+// span kernel records, per wavefront, the 100 MHz real-time counter at its
+// start, once x is staged and at its end, and the number of spans it
+// streamed, for the last launch.
+constexpr int kWaveTimesMax = 16384;
+__device__ uint64_t wave_times[kWaveTimesMax * 4];
+
+__device__ __forceinline__ void wave_times_record(int gw, uint64_t t0, uint64_t t1, int spans) {
+  const uint64_t t2 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x % kWave == 0 && gw < kWaveTimesMax) {
+    uint64_t* r = wave_times + 4 * (size_t)gw;
+    r[0] = t0;
+    r[1] = t1;
+    r[2] = t2;
+    r[3] = (uint64_t)spans;
+  }
+}
+#endif
+
 // How a span kernel keeps loads in flight while it computes.
 enum SpanPipe : int {
   kSpanSerial = 0,  // load a span, then compute it (occupancy hides latency)
@@ -438,6 +458,9 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_span(
   const int lane = tid % kWave;
   const int gw = (int)blockIdx.x * NWV + __builtin_amdgcn_readfirstlane(tid / kWave);
   const int GW = (int)gridDim.x * NWV;
+#ifdef QG_WAVE_TIMES
+  const uint64_t wt_start = __builtin_amdgcn_s_memrealtime();
+#endif
   const int nb = K >> bs_log2;
   const int PS = (K >> 5) * 5;
   const uint32_t magic = vreg_const(0x64006400u);
@@ -494,6 +517,9 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_span(
       },
       [&] { load(bufA, gw < nspans ? gw : nspans - 1); });
   __syncthreads();
+#ifdef QG_WAVE_TIMES
+  const uint64_t wt_x = __builtin_amdgcn_s_memrealtime();
+#endif
 
   // Computes span s from `cur`; after the pieces u of every row have been
   // consumed, `done(u)` runs (the ring reloads them there).
@@ -620,6 +646,9 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_span(
       compute(bufA, s, nothing);
     }
   }
+#ifdef QG_WAVE_TIMES
+  wave_times_record(gw, wt_start, wt_x, gw < nspans ? (nspans - gw + GW - 1) / GW : 0);
+#endif
 }
 
 // Matrix-core variant for M >= 2 (where the v_dot2 path turns VALU-bound;
@@ -981,8 +1010,15 @@ constexpr int kSpanPipe = kSpanRing;
 // Pieces per lane and span (rows per span x pieces per row and lane).
 constexpr int kSpanRows = 4;
 
-// Span kernel launch: one resident round of workgroups (or fewer when the
-// spans run out first).
+// Span kernel launch: two resident rounds of workgroups (or fewer when the
+// spans run out first).  Wavefronts of the workgroups dispatched first on a
+// CU run ahead of the later ones (per-wave timestamps of the lm_head: with
+// one round the first wavefronts end after 22 us, the last after 57); with
+// two rounds the second round's workgroups take the CU slots of the ones that
+// end early, which measured 1% faster on the lm_head (55.9 -> 55.3 us); four
+// rounds 56.1 us, one span per wavefront (16 rounds) 65 us.
+constexpr int kSpanRounds = 2;
+
 template <int M, int R, int U, bool RAGGED>
 hipError_t launch_span(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* scales,
                        const uint8_t* zp, void* y, int64_t ldy, int y_type, int N, int K,
@@ -996,7 +1032,7 @@ hipError_t launch_span(const uint16_t* x, int64_t ldx, const uint8_t* w, const u
                  : int4_gemv_span<M, R, U, false, kSpanPipe, RAGGED>;
   const int cap = resident_workgroups(kern, kBlock, shmem);
   const int want = (nspans + kBlock / kWave - 1) / (kBlock / kWave);
-  const int grid = want < cap ? want : cap;
+  const int grid = want < cap * kSpanRounds ? want : cap * kSpanRounds;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), shmem, stream, x, ldx, w, scales, zp, zrow, y,
                      ldy, y_type, N, K, bs_log2, nspans, x_vec16);
   note_launch(kPathInt4Span, M, grid, kBlock, shmem);
@@ -1229,6 +1265,21 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
 }
 
 }  // namespace
+
+#ifdef QG_WAVE_TIMES
+// Copies the wave records of the last span-kernel launch (4 x uint64 per
+// wavefront: start, x staged, end, spans) to host memory; returns the number
+// of wavefronts copied, or -1.
+extern "C" __attribute__((visibility("default"))) int qg_wave_times_read(uint64_t* host,
+                                                                          int max_waves) {
+  const int n = max_waves < kWaveTimesMax ? max_waves : kWaveTimesMax;
+  if (host == nullptr || n <= 0) return -1;
+  if (hipMemcpyFromSymbol(host, HIP_SYMBOL(wave_times), (size_t)n * 4 * sizeof(uint64_t), 0,
+                          hipMemcpyDeviceToHost) != hipSuccess)
+    return -1;
+  return n;
+}
+#endif
 
 hipError_t launch_int4_gemv(const uint16_t* x, int64_t ldx, const uint8_t* w,
                             const uint16_t* scales, const uint8_t* zp, void* y, int64_t ldy,
