@@ -368,39 +368,52 @@ void q4k_gemv_persistent(
   // Plane tile (PL): entry e = c * R + r (chunk c, row r_begin + r) is read
   // from the plane in that order (consecutive lanes, consecutive rows of one
   // chunk) and stored at ptile[(r * C + c) * 2].  The host guarantees
-  // R * C <= NT * kPlaneSlots.  e / R through a binary32 reciprocal: exact
-  // for e < 2^22 (the quotient is never closer than 0.5 / R to an integer).
+  // R * C <= NT * kPlaneSlots; a thread takes entries tid, tid + NT, ... as
+  // long as any thread of the workgroup has one (a uniform bound).  (c, r) of
+  // entry tid comes from a binary32 reciprocal (exact for tid < 2^22: the
+  // quotient is never closer than 0.5 / R to an integer); each further slot
+  // adds NT = qn * R + rn entries without a division.
   const int C = K >> 5;
   const int R = r_end - r_begin;
   float2 pv[PL ? kPlaneSlots : 1];
+  int tc0 = 0, tr0 = 0, qn = 0, rn = 0, nslots = 0;
+  if constexpr (PL) {
+    tc0 = (int)(((float)tid + 0.5f) * (1.0f / (float)R));
+    tr0 = tid - tc0 * R;
+    qn = NT / R;
+    rn = NT - qn * R;
+    nslots = (R * C + NT - 1) / NT;
+  }
+  auto plane_next = [&](int& c, int& r) {
+    c += qn;
+    r += rn;
+    if (r >= R) {
+      r -= R;
+      ++c;
+    }
+  };
   auto plane_load = [&] {
     if constexpr (PL) {
-      const float rinv = 1.0f / (float)R;
+      int c = tc0, r = tr0;
 #pragma unroll
       for (int k = 0; k < kPlaneSlots; ++k) {
-        int e = tid + k * NT;
-        e = e < R * C ? e : R * C - 1;
-        const int c = (int)(((float)e + 0.5f) * rinv);
-        const int r = e - c * R;
-        pv[k] = load8f(dsc + ((uint32_t)c * (uint32_t)N + (uint32_t)(r_begin + r)));
+        if (k == nslots) break;
+        if (c < C) pv[k] = load8f(dsc + ((uint32_t)c * (uint32_t)N + (uint32_t)(r_begin + r)));
+        plane_next(c, r);
       }
     }
   };
   auto plane_store = [&] {
     if constexpr (PL) {
-      const float rinv = 1.0f / (float)R;
+      int c = tc0, r = tr0;
 #pragma unroll
       for (int k = 0; k < kPlaneSlots; ++k) {
-        const int e = tid + k * NT;
-        if (e < R * C) {
-          const int c = (int)(((float)e + 0.5f) * rinv);
-          const int r = e - c * R;
-          *reinterpret_cast<float2*>(ptile + 2 * (r * C + c)) = pv[k];
-        }
+        if (k == nslots) break;
+        if (c < C) *reinterpret_cast<float2*>(ptile + 2 * (r * C + c)) = pv[k];
+        plane_next(c, r);
       }
     }
   };
-
   if (x_vec16) {
     const int v4 = K >> 2;
     stage_slots<2>(
