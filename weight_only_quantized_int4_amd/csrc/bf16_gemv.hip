@@ -280,10 +280,11 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_general(
 // reads 64 contiguous bytes of 16 rows), which is exactly the B operand of
 // MFMA t over k = 128c + 32t .. +32.  bf16 products are exact and the 4
 // MFMAs of every item chain into one fp32 accumulator, so the loop carries no
-// vector ALU work beyond LDS addressing.  x is staged once per workgroup in
-// LDS (16-byte slots of 8 elements, XOR-swizzled by 4 * (row & 3) so the A
-// reads of rows 0..3 fall in distinct banks).  Tiles, the D-item register
-// ring and the SPLIT partial sums follow the int4 matrix-core kernel.
+// vector ALU work beyond LDS addressing.  x is staged in LDS (16-byte slots
+// of 8 elements, XOR-swizzled by 4 * (row & 3) so the A
+// reads of rows 0..3 fall in distinct banks; with SPLIT each wave stages the
+// slots of its own items).  Tiles, the D-item register ring and the SPLIT
+// partial sums follow the int4 matrix-core kernel.
 template <int M, bool SPLIT, int NW, int D>
 __global__ __launch_bounds__(NW * kWave) void bf16_gemv_mfma(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw,
@@ -322,26 +323,55 @@ __global__ __launch_bounds__(NW * kWave) void bf16_gemv_mfma(
 
   Item ring[D];
   int lt = t0, lc = cb;
-  stage_slots<4>(
-      tid, NW * kWave, M * S8,
-      [&](int t) {
-        const uint16_t* src = x + (t / S8) * ldx + (t % S8) * 8;
-        if (x_vec16) return *reinterpret_cast<const uint4*>(src);
-        return make_uint4(src[0] | ((uint32_t)src[1] << 16), src[2] | ((uint32_t)src[3] << 16),
-                          src[4] | ((uint32_t)src[5] << 16), src[6] | ((uint32_t)src[7] << 16));
-      },
-      [&](int t, uint4 v) {
-        const int m = t / S8;
-        xs[m * S8 + ((t - m * S8) ^ ((m & 3) << 2))] = v;
-      },
-      [&] {  // unconditional: rows past the end are clamped
+  auto load_slot = [&](const uint16_t* src) {
+    if (x_vec16) return *reinterpret_cast<const uint4*>(src);
+    return make_uint4(src[0] | ((uint32_t)src[1] << 16), src[2] | ((uint32_t)src[3] << 16),
+                      src[4] | ((uint32_t)src[5] << 16), src[6] | ((uint32_t)src[7] << 16));
+  };
+  auto fill_ring = [&] {  // unconditional: rows past the end are clamped
 #pragma unroll
-        for (int k = 0; k < D; ++k) {
-          issue(ring[k], lt, lc);
-          advance(lt, lc);
-        }
-      });
-  __syncthreads();
+    for (int k = 0; k < D; ++k) {
+      issue(ring[k], lt, lc);
+      advance(lt, lc);
+    }
+  };
+  // SPLIT: each wavefront stages only the x slots of its own items [cb, ce)
+  // (16 per item and row of x) and reads no others, as in the int4 kernel
+  // (1536 x 6912 M = 8 12.2 -> 10.6 us, M = 3 10.9 -> 9.9; 4096^2 M = 8
+  // 10.2 -> 9.4), except for more than 4 rows of x over fewer than 2 items
+  // per wavefront, where most lanes would idle in it (6912 x 1536 M = 8:
+  // 7.4 against 7.8 us).
+  if (SPLIT && !(M > 4 && C < 2 * NW)) {
+    const int ns = 16 * (ce - cb);
+    bool pending = true;
+    for (int r0 = 0; r0 < ns; r0 += kWave) {
+      const int r = r0 + lane < ns ? r0 + lane : ns - 1;
+      const int gi = 16 * cb + r;
+      uint4 v[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) v[m] = load_slot(x + m * ldx + gi * 8);
+      if (pending) {
+        __builtin_amdgcn_sched_barrier(0);
+        fill_ring();
+        __builtin_amdgcn_sched_barrier(0);
+        pending = false;
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) xs[m * S8 + (gi ^ ((m & 3) << 2))] = v[m];
+    }
+    // Lanes read slots that other lanes of the wavefront wrote.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  } else {
+    stage_slots<4>(
+        tid, NW * kWave, M * S8, [&](int t) { return load_slot(x + (t / S8) * ldx + (t % S8) * 8); },
+        [&](int t, uint4 v) {
+          const int m = t / S8;
+          xs[m * S8 + ((t - m * S8) ^ ((m & 3) << 2))] = v;
+        },
+        fill_ring);
+    __syncthreads();
+  }
 
   uint32_t aoff[4];
   const int arow = n < M ? n : n % M;

@@ -676,8 +676,9 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_span(
 // DG groups are in flight per lane (a register ring; each slot is refilled as
 // soon as it is consumed, unconditionally: past the last item the row and item
 // indices are clamped, so surplus loads re-read cached bytes).
-// x is staged once per workgroup in LDS in natural order (16-byte slots of 8
-// halves, pre-permuted like the nibble pairs); each row's slots are XOR-
+// x is staged in LDS in natural order (16-byte slots of 8 halves,
+// pre-permuted like the nibble pairs; with SPLIT each wave stages the slots
+// of its own items, otherwise the workgroup stages all); each row's slots are XOR-
 // swizzled by (row & 3) on the slot bits that the 4 lanes of a row vary, so
 // the A reads of rows 0..3 fall in distinct banks.  SPLIT: all NW waves of a
 // workgroup share one tile and split its items; the partial sums are added in
@@ -793,20 +794,48 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
 
   Group ring[DG];
   Cursor lc = {t0, 0, item_begin(0), item_end(0)};  // next group to load
-  {
+  auto fill_ring = [&] {  // unconditional: rows past the end are clamped
+#pragma unroll
+    for (int k = 0; k < DG; ++k) {
+      issue(ring[k], lc);
+      advance(lc);
+    }
+  };
+  if constexpr (SPLIT && !PHASED) {
+    // Each wavefront stages only the x slots of its own items (16 per item
+    // and row of x), the same for every tile it takes, and reads no others:
+    // no workgroup barrier precedes the first item and a wavefront waits for
+    // its own x only (measured against the whole workgroup staging all of x:
+    // 1536 x 6912 M = 8 9.0 -> 7.7 us, M = 4 7.6 -> 6.9; 4096^2 M = 8 7.2 ->
+    // 6.2; 11008 x 4096 M = 8 10.5 -> 9.2; bitwise the same results).
+    const int ib = item_begin(0), ns = 16 * (item_end(0) - ib);
+    bool pending = true;
+    for (int r0 = 0; r0 < ns; r0 += kWave) {
+      const int r = r0 + lane < ns ? r0 + lane : ns - 1;
+      const int gi = 16 * ib + r;
+      uint4 v[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) v[m] = load_x8(x + m * ldx + gi * 8, x_vec16);
+      if (pending) {
+        __builtin_amdgcn_sched_barrier(0);
+        fill_ring();
+        __builtin_amdgcn_sched_barrier(0);
+        pending = false;
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) xs[m * S8 + (gi ^ ((m & 3) << kSwzShift))] = pair_halves(v[m]);
+    }
+    // The wavefront's lanes read slots that other lanes of it wrote: keep
+    // the reads behind the writes (LDS serves one wavefront in order).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  } else {
     const int L8 = chunk_slots(0);
     stage_slots<kMfmaStageUnroll>(
         tid, NW * kWave, M * L8, [&](int t) { return stage_load(0, L8, t); },
-        [&](int t, uint4 v) { stage_store(L8, t, v); },
-        [&] {  // unconditional: rows past the end are clamped
-#pragma unroll
-          for (int k = 0; k < DG; ++k) {
-            issue(ring[k], lc);
-            advance(lc);
-          }
-        });
+        [&](int t, uint4 v) { stage_store(L8, t, v); }, fill_ring);
+    __syncthreads();
   }
-  __syncthreads();
 
   // LDS byte address of the A slot that MFMA t of item 0 reads (rows >= M
   // read row n % M).
