@@ -12,7 +12,7 @@
 //    wavefront load instruction reads 64/LPR contiguous runs of LPR*16 bytes.
 //    Each lane owns R rows at once so that every x value read from LDS is
 //    used R times.
-//  * x is staged once per workgroup in LDS, pre-permuted within every group of
+//  * x is staged in LDS (once per workgroup), pre-permuted within every group of
 //    8 elements to (x0,x4 | x1,x5 | x2,x6 | x3,x7) so that it lines up with the
 //    nibble pairs below.  Each 64-byte piece of x is followed by 16 bytes of
 //    padding: the lanes of a row read pieces 80 bytes apart, which spreads
@@ -31,11 +31,14 @@
 //  * Reduction: the LPR lanes of a row reduce with cross-lane shuffles; no
 //    atomics and no cross-workgroup split-K (the AstrAI commit list measured
 //    split-K as a regression).
-//  * Single rows of 2048, 4096 or 8192 weights (the lm_head and the 4096-wide
-//    layers at M = 1) take the span kernel instead: each wavefront streams
-//    whole 4 KB runs of consecutive rows, one contiguous 1 KB access per load
-//    instruction, and reloads each piece's registers with the next run as soon
-//    as they are consumed.
+//  * At M = 1, rows of 2048, 4096 or 8192 weights (the lm_head and the
+//    4096-wide layers) and the rows of matrices too short for the persistent
+//    kernel (128 < K/32 <= 512) take the span kernel instead: each wavefront
+//    streams whole runs of about 4 KB of consecutive rows, one contiguous 1 KB
+//    access per load instruction, and reloads each piece's registers with the
+//    next run as soon as they are consumed.
+//  * M >= 2 takes the matrix cores (int4_gemv_mfma below), except a few
+//    M = 2 shapes.
 #include <type_traits>
 
 #include "int4_device.h"
