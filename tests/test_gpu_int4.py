@@ -468,3 +468,53 @@ def test_random_shapes_and_strides(case):
     y = _run(p, M, out_dtype, x=xd, ldy=ldy)
     yr, S = oracle.int4_gemv(xrows, p.w, p.scales, p.zp, M, N, K, bs, ldx=ldx)
     assert_accept(y_host(y), yr, S, OUT_NAME[out_dtype], f"int4 random case {case} ({q.last_launch()})")
+
+
+# k parts of the split matrix-core kernel: where 16-row tiles leave CUs idle,
+# the MFMA columns carry 8 rows in 2 parts of their k range (M <= 8) or 4 rows
+# in 4 parts (M <= 4); the grid is one workgroup per tile of 16 / ks rows.
+@pytest.mark.parametrize("N,K,bs,asym,M,ks", [(1000, 4096, 32, True, 3, 4),
+                                              (1003, 4096, 64, True, 4, 4),
+                                              (1003, 4096, 128, False, 4, 4),
+                                              (777, 2048, 256, True, 6, 2),
+                                              (250, 8192, 32, True, 5, 2),
+                                              (1001, 2048, 64, True, 8, 2),
+                                              (1536, 6912, 128, False, 7, 2)])
+def test_matrix_core_k_parts(N, K, bs, asym, M, ks):
+    say(f"int4 matrix-core k parts N={N} K={K} bs={bs} asym={asym} M={M} ks={ks}")
+    p = int4_case(N, K, bs, asym, 1500 + M)
+    y = y_host(_run(p, M, torch.float32))
+    tr = 16 // ks
+    assert f"int4_mfma_split M={M} grid={(N + tr - 1) // tr} " in q.last_launch(), q.last_launch()
+    yr, S = int4_ref(N, K, bs, asym, 1500 + M)
+    assert_accept(y, yr[:M], S[:M], "f32", f"int4 k parts {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("K,bs,M,ks", [(4096, 32, 4, 4), (4096, 64, 3, 4), (4096, 256, 4, 4),
+                                       (2048, 32, 8, 2), (2048, 128, 5, 2)])
+def test_one_hot_probe_k_parts_is_bit_exact(K, bs, M, ks):
+    """Row r of x is one-hot at k_r (positions across every item and at item
+    seams, so every part of every step is probed); y[r, n] must equal the
+    oracle's dequantized w[n, k_r] bitwise (fp32 out)."""
+    N = 203
+    p = int4_case(N, K, bs, True, 35)
+    wdq = oracle.int4_dequant(p.w, p.scales, p.zp, N, K, bs)
+    wd, sd, zd = to_dev(p.w), f16_dev(p.scales), to_dev(p.zp)
+    kpos = sorted(set(list(range(0, K, 29)) + [128 * i - 1 for i in range(1, K // 128)] +
+                      [128 * i for i in range(K // 128)] + [K - 1]))
+    say(f"int4 k-parts one-hot probe K={K} bs={bs} M={M}: {len(kpos)} positions")
+    tr = 16 // ks
+    for i0 in range(0, len(kpos), M):
+        kk = kpos[i0:i0 + M]
+        kk = kk + [kk[-1]] * (M - len(kk))
+        x = torch.zeros((M, K), dtype=torch.float16, device=DEV)
+        for r, k in enumerate(kk):
+            x[r, k] = 1.0
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        q.qgemv_int4_blockwise(x, wd, sd, zd, y, bs)
+        assert f"int4_mfma_split M={M} grid={(N + tr - 1) // tr} " in q.last_launch(), q.last_launch()
+        got = y.cpu().numpy()
+        want = wdq[:, kk].T.astype(np.float32)
+        assert np.array_equal(got, want), kk
+        nz = want != 0
+        assert np.array_equal(got.view(np.uint32)[nz], want.view(np.uint32)[nz]), kk

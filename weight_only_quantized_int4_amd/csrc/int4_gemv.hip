@@ -692,11 +692,22 @@ __global__ __launch_bounds__(kBlock) void int4_gemv_span(
 // between chunks.
 // D needs no cross-lane reduction: lane (n, g) ends with rows 4g..4g+3 of
 // column n.
+// KS (k parts, with SPLIT and x wholly staged; M <= 16 / KS): A rows M..15
+// would idle, so the 16 MFMA columns carry TR = 16 / KS weight rows in KS
+// parts of their k range instead of 16 rows: column n is tile row n % TR,
+// part h = n / TR, and A row r holds x row r % TR (repeated past M) of part
+// r / TR.  A step s of a tile covers items KS * s + h of its rows (the host
+// takes KS only where it divides the row's item count), and D[r][n] is a
+// partial sum of output (r % TR, n % TR) exactly where r / TR = h; the other
+// entries are computed and never read.  A short matrix then spreads over KS
+// times as many workgroups (1536 rows: 96 tiles of 16 rows, 192 of 8 rows),
+// with no data shared between workgroups; the tile-end sum adds the KS parts
+// after the waves, in a fixed order.
 // x slots each thread loads before it stores them (matrix-core kernel;
 // measured on the 4096-row 7B layers: 12 and 16 are slower).
 constexpr int kMfmaStageUnroll = 4;
 
-template <int M, bool ZP, int PPB, bool SPLIT, int NW, int DG, bool PHASED = false>
+template <int M, bool ZP, int PPB, bool SPLIT, int NW, int DG, bool PHASED = false, int KS = 1>
 __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ w,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zp, int zrow,
@@ -704,26 +715,32 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     int x_vec16, int cp) {
   static_assert(!PHASED || SPLIT, "chunks of x are staged per tile: split mode only");
   static_assert(PPB == 1 || PPB == 2 || PPB == 4, "pieces per scale block");
+  static_assert(KS == 1 || ((KS == 2 || KS == 4) && SPLIT && !PHASED && M <= 16 / KS),
+                "k parts: split tiles with x wholly staged, M rows per part");
+  constexpr int TR = 16 / KS;  // weight rows per tile
   extern __shared__ uint4 xs[];  // [M][CP*16] slots, swizzled; then the SPLIT partials
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = lane & 15, g = lane >> 4;
+  const int ti = n % TR, h = n / TR;  // tile row and k part of column n
   const int nb = K >> bs_log2;
   const int C = K >> 7;                                // items per row
-  const int CP = PHASED ? cp : C;                      // items per staged chunk of x
-  const int nph = PHASED ? (C + CP - 1) / CP : 1;      // chunks
-  const int S8 = CP << 4;                              // 16-byte slots per staged x row
-  // This wave's stream of tiles (t0, t0 + TS, ...) and its item range
-  // [item_begin(p), item_end(p)) in chunk p of each tile.
+  const int CS = C / KS;                               // steps per tile
+  const int CP = PHASED ? cp : CS;                     // steps per staged chunk of x
+  const int nph = PHASED ? (CS + CP - 1) / CP : 1;     // chunks
+  const int S8 = (CP * KS) << 4;                       // 16-byte slots per staged x row
+  // This wave's stream of tiles (t0, t0 + TS, ...) and its step range
+  // [item_begin(p), item_end(p)) in chunk p of each tile (with KS = 1 a step
+  // is an item).
   const int t0 = SPLIT ? (int)blockIdx.x : (int)blockIdx.x * NW + wave;
   const int TS = SPLIT ? (int)gridDim.x : (int)gridDim.x * NW;
   auto item_begin = [&](int p) {
-    const int base = p * CP, len = (C - base < CP ? C - base : CP);
+    const int base = p * CP, len = (CS - base < CP ? CS - base : CP);
     return SPLIT ? base + wave * len / NW : base;
   };
   auto item_end = [&](int p) {
-    const int base = p * CP, len = (C - base < CP ? C - base : CP);
+    const int base = p * CP, len = (CS - base < CP ? CS - base : CP);
     return SPLIT ? base + (wave + 1) * len / NW : base + len;
   };
   const int my_tiles = t0 < ntiles ? (ntiles - t0 + TS - 1) / TS : 0;
@@ -738,9 +755,9 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
   // Scale bytes of one item: 8 (PPB 1: four blocks), 4 (two) or 2 (one).
   using SType = std::conditional_t<PPB == 1, uint2, uint32_t>;
   struct Group {
-    uint4 w[4];  // item j: piece 4(gc+j)+g of row n
-    SType s;     // scales of item gc+g
-    uint32_t z;  // zero-point bytes of item gc+g (PPB 1: 2 bytes, else 1)
+    uint4 w[4];  // step j: piece 4(KS(gc+j)+h)+g of tile row ti
+    SType s;     // scales of step gc+g
+    uint32_t z;  // zero-point bytes of step gc+g (PPB 1: 2 bytes, else 1)
   };
   // Position in the stream: tile, chunk, first item of the group, end of the
   // wave's items in that chunk.
@@ -750,15 +767,15 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
   const char* sbytes = reinterpret_cast<const char*>(scales);
   auto issue = [&](Group& gr, const Cursor& cu) {
     const int gc = cu.gc, ce = cu.e;
-    const int row = cu.tile * 16 + n;
+    const int row = cu.tile * TR + ti;
     const uint32_t nl = (uint32_t)(row < N ? row : N - 1);
     const uint32_t wrow = nl * (uint32_t)(K >> 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = gc + j < ce ? gc + j : ce - 1;
+      const int c = KS * (gc + j < ce ? gc + j : ce - 1) + h;
       gr.w[j] = load16(w + (wrow + (uint32_t)(4 * c + g) * 16u));
     }
-    const int cg = gc + g < ce ? gc + g : ce - 1;
+    const int cg = KS * (gc + g < ce ? gc + g : ce - 1) + h;
     const uint32_t blk0 = (uint32_t)((cg << 7) >> bs_log2);  // first block of item cg
     const char* sp = sbytes + (nl * (uint32_t)nb + blk0) * 2u;
     if constexpr (PPB == 1) gr.s = *reinterpret_cast<const uint2*>(sp);
@@ -793,7 +810,7 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     const int gi = t - m * L8;
     xs[m * S8 + (gi ^ ((m & 3) << kSwzShift))] = pair_halves(v);
   };
-  auto chunk_slots = [&](int p) { return (C - p * CP < CP ? C - p * CP : CP) << 4; };
+  auto chunk_slots = [&](int p) { return (CS - p * CP < CP ? CS - p * CP : CP) << 4; };
 
   Group ring[DG];
   Cursor lc = {t0, 0, item_begin(0), item_end(0)};  // next group to load
@@ -811,7 +828,7 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     // its own x only (measured against the whole workgroup staging all of x:
     // 1536 x 6912 M = 8 9.0 -> 7.7 us, M = 4 7.6 -> 6.9; 4096^2 M = 8 7.2 ->
     // 6.2; 11008 x 4096 M = 8 10.5 -> 9.2; bitwise the same results).
-    const int ib = item_begin(0), ns = 16 * (item_end(0) - ib);
+    const int ib = KS * item_begin(0), ns = 16 * KS * (item_end(0) - item_begin(0));
     bool pending = true;
     for (int r0 = 0; r0 < ns; r0 += kWave) {
       const int r = r0 + lane < ns ? r0 + lane : ns - 1;
@@ -840,14 +857,14 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     __syncthreads();
   }
 
-  // LDS byte address of the A slot that MFMA t of item 0 reads (rows >= M
-  // read row n % M).
+  // LDS byte address of the A slot that MFMA t of step 0 reads: A row n is
+  // x row n % TR (rows >= M read row (n % TR) % M) at item h.
   uint32_t aoff[4];
-  const int arow = n < M ? n : n % M;
+  const int arow = ti < M ? ti : ti % M;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int slot = PPB == 4 ? 4 * g + t : 4 * t + g;
-    aoff[t] = (uint32_t)((arow * S8 + (slot ^ ((arow & 3) << kSwzShift))) * 16);
+    aoff[t] = (uint32_t)((arow * S8 + 16 * h + (slot ^ ((arow & 3) << kSwzShift))) * 16);
   }
   const char* xs_bytes = reinterpret_cast<const char*>(xs);
 
@@ -878,7 +895,7 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
     for (int j = 0; j < 4; ++j) {
       const int c = gc + j;
       if (c >= ce) break;  // partial last group of a tile (uniform)
-      const uint32_t ibase = (uint32_t)(c - cu.p * CP) * 256u;
+      const uint32_t ibase = (uint32_t)(KS * (c - cu.p * CP)) * 256u;
       uint4 av[4];  // A operands of the item's 4 MFMAs
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -905,7 +922,7 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
         if constexpr (!ZP) {
           return 8u;
         } else if constexpr (PPB == 4) {
-          const uint32_t blk0 = (uint32_t)((c << 7) >> bs_log2);
+          const uint32_t blk0 = (uint32_t)(((KS * c + h) << 7) >> bs_log2);
           return (zb[j] >> ((blk0 & 1u) << 2)) & 15u;
         } else {
           return (zb[j] >> (4 * b)) & 15u;
@@ -944,18 +961,32 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
             [&](int t, uint4 v) { stage_store(L8, t, v); });
         __syncthreads();
       } else if (c == ce - 1) {  // tile finished: lane (n, g) holds rows 4g..4g+3 of column n
-        const int row = tile * 16 + n;
+        const int row = tile * TR + ti;
         if constexpr (SPLIT) {
           f32x4* red = reinterpret_cast<f32x4*>(xs + M * S8);  // [NW][64]
           red[wave * kWave + lane] = acc;
           __syncthreads();
-          if (wave == 0) {
-            f32x4 sum = red[lane];
+          // Part 0's lanes (n < TR, rows 4g.. < TR) add each part's sum over
+          // the waves, parts in order; part h of the same outputs sits in
+          // lane (n + h * TR, g + h * TR / 4).
+          if (wave == 0 && (KS == 1 || (h == 0 && 4 * g < TR))) {
+            auto part_sum = [&](int src) {
+              f32x4 ps = red[src];
 #pragma unroll
-            for (int v = 1; v < NW; ++v) {
-              const f32x4 o = red[v * kWave + lane];
+              for (int v = 1; v < NW; ++v) {
+                const f32x4 o = red[v * kWave + src];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) sum[i] += o[i];
+                for (int i = 0; i < 4; ++i) ps[i] += o[i];
+              }
+              return ps;
+            };
+            f32x4 sum = part_sum(lane);
+            // a loop, so that one part's reads are in registers at a time
+#pragma unroll 1
+            for (int hp = 1; hp < KS; ++hp) {
+              const f32x4 ps = part_sum(lane + hp * (TR + 16 * (TR / 4)));
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sum[i] += ps[i];
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1123,19 +1154,20 @@ constexpr int kMfmaDepth = 1;
 constexpr int kSplitWaves = 8;
 constexpr int kSplitDepth = 1;
 
-template <int M, int PPB, bool SPLIT, bool PHASED = false>
+template <int M, int PPB, bool SPLIT, bool PHASED = false, int KS = 1>
 hipError_t launch_mfma_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w,
                            const uint16_t* scales, const uint8_t* zp, void* y, int64_t ldy,
                            int y_type, int N, int K, int block_size, size_t shmem, int cp,
                            hipStream_t stream) {
   constexpr int NW = SPLIT ? kSplitWaves : kMfmaWaves;
   constexpr int DG = SPLIT ? kSplitDepth : kMfmaDepth;
+  constexpr int TR = 16 / KS;
   const int bs_log2 = __builtin_ctz((unsigned)block_size);
   const int zrow = ((K / block_size) + 1) / 2;
   const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
-  const int ntiles = (N + 15) / 16;
-  auto kern = zp ? int4_gemv_mfma<M, true, PPB, SPLIT, NW, DG, PHASED>
-                 : int4_gemv_mfma<M, false, PPB, SPLIT, NW, DG, PHASED>;
+  const int ntiles = (N + TR - 1) / TR;
+  auto kern = zp ? int4_gemv_mfma<M, true, PPB, SPLIT, NW, DG, PHASED, KS>
+                 : int4_gemv_mfma<M, false, PPB, SPLIT, NW, DG, PHASED, KS>;
   const hipError_t e = allow_lds(kern, shmem);
   if (e != hipSuccess) return e;
   // Phased: one tile per workgroup (the chunks of x are staged per tile).
@@ -1164,6 +1196,35 @@ inline int mfma_chunk_items(int M, int K) {
   return C - (nph - 1) * cp >= NW ? cp : 0;
 }
 
+// CUs of the current device (cached per device).
+inline int device_cus() {
+  static std::mutex mu;
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// k parts of the split matrix-core kernel: 1, or 2 (4) when 16-row (8-row)
+// tiles number fewer than the CUs, the parts divide the row's items, every
+// wave keeps at least one step, and M fits the A rows of a part.
+inline int mfma_k_parts(int M, int N, int K) {
+  const int C = K / 128, cus = device_cus();
+  int ks = 1;
+  while (ks < 4 && (N + 16 / ks - 1) / (16 / ks) < cus && M <= 8 / ks && C % (2 * ks) == 0 &&
+         C / (2 * ks) >= kSplitWaves)
+    ks *= 2;
+  return ks;
+}
+
 // Whole tiles per wave when the tiles fill at least half of the resident
 // wavefront slots; otherwise (and when every wave gets at least one item and
 // the partial sums fit in LDS) the waves of a workgroup split each tile.
@@ -1187,9 +1248,24 @@ hipError_t launch_mfma_ppb(const uint16_t* x, int64_t ldx, const uint8_t* w,
   }
   const bool few_tiles = !x_fits || 2LL * ntiles < waves;
   if (few_tiles && K / 128 >= kSplitWaves) {
-    if (split_bytes <= (size_t)kLdsMax)
+    if (split_bytes <= (size_t)kLdsMax) {
+      // k parts: tiles of 8 (4) rows when 16-row tiles leave CUs idle
+      switch (mfma_k_parts(M, N, K)) {
+        case 4:
+          if constexpr (M <= 4)
+            return launch_mfma_cfg<M, PPB, true, false, 4>(x, ldx, w, scales, zp, y, ldy, y_type,
+                                                           N, K, block_size, split_bytes, 0,
+                                                           stream);
+          break;
+        case 2:
+          return launch_mfma_cfg<M, PPB, true, false, 2>(x, ldx, w, scales, zp, y, ldy, y_type, N,
+                                                         K, block_size, split_bytes, 0, stream);
+        default:
+          break;
+      }
       return launch_mfma_cfg<M, PPB, true>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
                                            block_size, split_bytes, K / 128, stream);
+    }
     const int cp = mfma_chunk_items(M, K);
     if (cp != 0)
       return launch_mfma_cfg<M, PPB, true, true>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
