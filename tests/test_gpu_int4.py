@@ -491,7 +491,8 @@ def test_matrix_core_k_parts(N, K, bs, asym, M, ks):
 
 
 @pytest.mark.parametrize("K,bs,M,ks", [(4096, 32, 4, 4), (4096, 64, 3, 4), (4096, 256, 4, 4),
-                                       (2048, 32, 8, 2), (2048, 128, 5, 2)])
+                                       (2048, 32, 8, 2), (2048, 128, 5, 2), (8192, 64, 4, 4),
+                                       (8192, 32, 6, 2)])
 def test_one_hot_probe_k_parts_is_bit_exact(K, bs, M, ks):
     """Row r of x is one-hot at k_r (positions across every item and at item
     seams, so every part of every step is probed); y[r, n] must equal the

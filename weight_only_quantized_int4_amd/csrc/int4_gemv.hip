@@ -1196,23 +1196,6 @@ inline int mfma_chunk_items(int M, int K) {
   return C - (nph - 1) * cp >= NW ? cp : 0;
 }
 
-// CUs of the current device (cached per device).
-inline int device_cus() {
-  static std::mutex mu;
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1)
-      cus = 256;
-    cached[dev] = cus;
-  }
-  return cached[dev];
-}
-
 // k parts of the split matrix-core kernel: 1, or 2 (4) when 16-row (8-row)
 // tiles number fewer than the CUs, the parts divide the row's items, every
 // wave keeps at least one step, and M fits the A rows of a part.
@@ -1249,7 +1232,10 @@ hipError_t launch_mfma_ppb(const uint16_t* x, int64_t ldx, const uint8_t* w,
   const bool few_tiles = !x_fits || 2LL * ntiles < waves;
   if (few_tiles && K / 128 >= kSplitWaves) {
     if (split_bytes <= (size_t)kLdsMax) {
-      // k parts: tiles of 8 (4) rows when 16-row tiles leave CUs idle
+      // k parts: tiles of 8 (4) rows when 16-row tiles leave CUs idle (8
+      // wavefronts per workgroup: 16 measured slower, 1536 x 6912 at M = 8
+      // 7.9 against 6.2 us; so did k parts in the packed layout's kernel,
+      // 7.0 against 6.8 us for its 16-row tiles over 16 wavefronts)
       switch (mfma_k_parts(M, N, K)) {
         case 4:
           if constexpr (M <= 4)

@@ -140,6 +140,23 @@ inline int resident_workgroups(F kernel, int threads, size_t shmem) {
   return value;
 }
 
+// CUs of the current device (cached per device).
+inline int device_cus() {
+  static std::mutex mu;
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 // Raise `kernel`'s dynamic-LDS limit to `bytes` when that is above 64 KB
 // (once per kernel, device and size).
 template <typename F>
