@@ -246,3 +246,45 @@ def test_random_shapes_offsets_and_strides(case):
     q.gemv_bf16(xd, wd, y)
     yr, S = _ref(p, M, ldw=ldw, wbuf=wrows, xbuf=xrows, ldx=ldx)
     assert_accept(y_host(y), yr, S, "f32", f"bf16 random case {case}")
+
+
+# k parts of the split matrix-core kernel: where 16-row tiles leave CUs idle,
+# the MFMA columns carry 8 rows in 2 parts of their k range (M <= 8) or 4
+# rows in 4 parts (M <= 4); one workgroup per tile of 16 / ks rows.
+@pytest.mark.parametrize("N,K,M,ks", [(1536, 6912, 3, 2), (1003, 4096, 4, 4), (777, 2048, 6, 2),
+                                      (1001, 2048, 8, 2), (203, 4096, 2, 4), (250, 8192, 5, 2)])
+def test_matrix_core_k_parts(N, K, M, ks):
+    p = bf16_case(N, K, 390 + M)
+    say(f"bf16 k parts N={N} K={K} M={M} ks={ks}")
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    q.gemv_bf16(bf16_dev(p.x[:M]), bf16_dev(p.w), y)
+    tr = 16 // ks
+    assert f"bf16_mfma_split M={M} grid={(N + tr - 1) // tr} " in q.last_launch(), q.last_launch()
+    yr, S = _ref(p, M)
+    assert_accept(y_host(y), yr, S, "f32", f"bf16 k parts {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("K,M,ks", [(4096, 4, 4), (4096, 3, 4), (2048, 8, 2), (8192, 5, 2)])
+def test_one_hot_probe_k_parts_is_bit_exact(K, M, ks):
+    """Row r of x one-hot at k_r (every 128-wide item and its seams probed, so
+    every part of every step): y[r, n] must equal the oracle's y, which is
+    w[n, k_r] exactly (fp32 out)."""
+    N = 203
+    p = bf16_case(N, K, 395 + M)
+    wd = bf16_dev(p.w)
+    kpos = sorted(set(list(range(0, K, 29)) + [128 * i - 1 for i in range(1, K // 128)] +
+                      [128 * i for i in range(K // 128)] + [K - 1]))
+    x_all, want_all = _one_hot_expected(p, kpos)
+    say(f"bf16 k-parts one-hot K={K} M={M}: {len(kpos)} positions")
+    tr = 16 // ks
+    for i0 in range(0, len(kpos), M):
+        rows = list(range(i0, min(i0 + M, len(kpos))))
+        rows = rows + [rows[-1]] * (M - len(rows))
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        q.gemv_bf16(bf16_dev(x_all[rows]), wd, y)
+        assert f"bf16_mfma_split M={M} grid={(N + tr - 1) // tr} " in q.last_launch(), q.last_launch()
+        got = y.cpu().numpy()
+        want = want_all[rows]
+        assert np.array_equal(got, want), rows
+        nz = want != 0
+        assert np.array_equal(got.view(np.uint32)[nz], want.view(np.uint32)[nz]), rows

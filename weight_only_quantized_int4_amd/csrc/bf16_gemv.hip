@@ -284,22 +284,32 @@ __global__ __launch_bounds__(kBlock) void bf16_gemv_general(
 // of 8 elements, XOR-swizzled by 4 * (row & 3) so the A
 // reads of rows 0..3 fall in distinct banks; with SPLIT each wave stages the
 // slots of its own items).  Tiles, the D-item register ring and the SPLIT
-// partial sums follow the int4 matrix-core kernel.
-template <int M, bool SPLIT, int NW, int D>
+// partial sums follow the int4 matrix-core kernel, and so do the k parts
+// (KS, with SPLIT): where 16-row tiles leave CUs idle, the 16 MFMA columns
+// carry TR = 16 / KS rows in KS parts of their k range (column n: tile row
+// n % TR, part h = n / TR; A row r: x row r % TR of part r / TR; step c
+// covers items KS * c + h), and the tile-end sum adds the parts after the
+// wavefronts, in a fixed order.
+template <int M, bool SPLIT, int NW, int D, int KS = 1>
 __global__ __launch_bounds__(NW * kWave) void bf16_gemv_mfma(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w, int64_t ldw,
     void* __restrict__ y, int64_t ldy, int y_type, int N, int K, int ntiles, int x_vec16) {
+  static_assert(KS == 1 || ((KS == 2 || KS == 4) && SPLIT && M <= 16 / KS),
+                "k parts: split tiles, M rows per part");
+  constexpr int TR = 16 / KS;  // weight rows per tile
   extern __shared__ uint4 xs[];  // [M][K/8] slots, swizzled; then the SPLIT partials
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = lane & 15, g = lane >> 4;
+  const int ti = n % TR, h = n / TR;  // tile row and k part of column n
   const int S8 = K >> 3;
   const int C = K >> 7;
+  const int CS = C / KS;  // steps per tile
   const int t0 = SPLIT ? (int)blockIdx.x : (int)blockIdx.x * NW + wave;
   const int TS = SPLIT ? (int)gridDim.x : (int)gridDim.x * NW;
-  const int cb = SPLIT ? wave * C / NW : 0;
-  const int ce = SPLIT ? (wave + 1) * C / NW : C;
+  const int cb = SPLIT ? wave * CS / NW : 0;
+  const int ce = SPLIT ? (wave + 1) * CS / NW : CS;
   const int my_tiles = t0 < ntiles ? (ntiles - t0 + TS - 1) / TS : 0;
   const int nitems = my_tiles * (ce - cb);
 
@@ -308,11 +318,11 @@ __global__ __launch_bounds__(NW * kWave) void bf16_gemv_mfma(
   };
   const uint8_t* wb = reinterpret_cast<const uint8_t*>(w);
   auto issue = [&](Item& it, int tile, int c) {
-    const int row = tile * 16 + n;
+    const int row = tile * TR + ti;
     // byte offset (tensors are below 4 GiB): a 32-bit offset off a uniform
     // base keeps each load to one address register
-    const uint32_t base =
-        ((uint32_t)(row < N ? row : N - 1) * (uint32_t)ldw + (uint32_t)(128 * c + 8 * g)) * 2u;
+    const uint32_t base = ((uint32_t)(row < N ? row : N - 1) * (uint32_t)ldw +
+                           (uint32_t)(128 * (KS * c + h) + 8 * g)) * 2u;
 #pragma unroll
     for (int t = 0; t < 4; ++t) it.w[t] = load16(wb + (base + 64u * t));
   };
@@ -342,11 +352,11 @@ __global__ __launch_bounds__(NW * kWave) void bf16_gemv_mfma(
   // per wavefront, where most lanes would idle in it (6912 x 1536 M = 8:
   // 7.4 against 7.8 us).
   if (SPLIT && !(M > 4 && C < 2 * NW)) {
-    const int ns = 16 * (ce - cb);
+    const int ns = 16 * KS * (ce - cb);
     bool pending = true;
     for (int r0 = 0; r0 < ns; r0 += kWave) {
       const int r = r0 + lane < ns ? r0 + lane : ns - 1;
-      const int gi = 16 * cb + r;
+      const int gi = 16 * KS * cb + r;
       uint4 v[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) v[m] = load_slot(x + m * ldx + gi * 8);
@@ -374,16 +384,16 @@ __global__ __launch_bounds__(NW * kWave) void bf16_gemv_mfma(
   }
 
   uint32_t aoff[4];
-  const int arow = n < M ? n : n % M;
+  const int arow = ti < M ? ti : ti % M;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    aoff[t] = (uint32_t)((arow * S8 + ((4 * t + g) ^ ((arow & 3) << 2))) * 16);
+    aoff[t] = (uint32_t)((arow * S8 + 16 * h + ((4 * t + g) ^ ((arow & 3) << 2))) * 16);
   const char* xs_bytes = reinterpret_cast<const char*>(xs);
 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc = zero4;
   auto consume = [&](const Item& cur, int tile, int c) {
-    const uint32_t ibase = (uint32_t)c * 256u;
+    const uint32_t ibase = (uint32_t)(KS * c) * 256u;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint4 a = *reinterpret_cast<const uint4*>(xs_bytes + (aoff[t] + ibase));
@@ -391,18 +401,38 @@ __global__ __launch_bounds__(NW * kWave) void bf16_gemv_mfma(
                                                     acc, 0, 0, 0);
     }
     if (c == ce - 1) {  // tile finished: lane (n, g) holds rows 4g..4g+3 of column n
-      const int row = tile * 16 + n;
+      const int row = tile * TR + ti;
       if constexpr (SPLIT) {
         f32x4* red = reinterpret_cast<f32x4*>(xs + M * S8);  // [NW][64]
         red[wave * kWave + lane] = acc;
         __syncthreads();
-        if (wave == 0) {
-          f32x4 sum = red[lane];
+        // Part 0's lanes (n < TR, rows 4g.. < TR) add each part's sum over
+        // the waves, parts in order; part h of the same outputs sits in
+        // lane (n + h * TR, g + h * TR / 4).
+        if (wave == 0 && (KS == 1 || (h == 0 && 4 * g < TR))) {
+          auto part_sum = [&](int src) {
+            f32x4 ps = red[src];
 #pragma unroll
-          for (int v = 1; v < NW; ++v) {
-            const f32x4 o = red[v * kWave + lane];
+            for (int v = 1; v < NW; ++v) {
+              const f32x4 o = red[v * kWave + src];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sum[i] += o[i];
+              for (int i = 0; i < 4; ++i) ps[i] += o[i];
+            }
+            return ps;
+          };
+          f32x4 sum = part_sum(lane);
+          // a loop (its count hidden from the compiler, which would otherwise
+          // peel a single pass), so that one part's reads are in registers at
+          // a time
+          if constexpr (KS > 1) {
+            int nparts = KS;
+            asm volatile("" : "+s"(nparts));
+#pragma unroll 1
+            for (int hp = 1; hp < nparts; ++hp) {
+              const f32x4 ps = part_sum(lane + hp * (TR + 16 * (TR / 4)));
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sum[i] += ps[i];
+            }
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -454,13 +484,13 @@ constexpr int kMfmaDepth = 2;
 constexpr int kSplitWaves = 8;
 constexpr int kSplitDepth = 2;
 
-template <int M, bool SPLIT, int NW, int D>
+template <int M, bool SPLIT, int NW, int D, int KS = 1>
 hipError_t launch_mfma_cfg(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, void* y,
                            int64_t ldy, int y_type, int N, int K, size_t shmem,
                            hipStream_t stream) {
   const int x_vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0) && (ldx % 8 == 0);
-  const int ntiles = (N + 15) / 16;
-  auto kern = bf16_gemv_mfma<M, SPLIT, NW, D>;
+  const int ntiles = (N + 16 / KS - 1) / (16 / KS);
+  auto kern = bf16_gemv_mfma<M, SPLIT, NW, D, KS>;
   const hipError_t e = allow_lds(kern, shmem);
   if (e != hipSuccess) return e;
   const int cap = resident_workgroups(kern, NW * kWave, shmem);
@@ -486,9 +516,25 @@ hipError_t launch_mfma(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_
   // Split: every wave needs at least one item of the tile, and the partial
   // sums (16 bytes per lane) share LDS with x.
   const size_t split_bytes = xbytes + (size_t)kSplitWaves * kWave * 16;
-  if (2LL * ntiles < waves && K / 128 >= kSplitWaves && split_bytes <= (size_t)kLdsMax)
+  if (2LL * ntiles < waves && K / 128 >= kSplitWaves && split_bytes <= (size_t)kLdsMax) {
+    // k parts: tiles of 8 (4) rows when 16-row tiles leave CUs idle
+    switch (mfma_k_parts(M, N, K, kSplitWaves)) {
+      case 4:
+        if constexpr (M <= 4)
+          return launch_mfma_cfg<M, true, kSplitWaves, kSplitDepth, 4>(x, ldx, w, ldw, y, ldy,
+                                                                      y_type, N, K, split_bytes,
+                                                                      stream);
+        break;
+      case 2:
+        return launch_mfma_cfg<M, true, kSplitWaves, kSplitDepth, 2>(x, ldx, w, ldw, y, ldy,
+                                                                    y_type, N, K, split_bytes,
+                                                                    stream);
+      default:
+        break;
+    }
     return launch_mfma_cfg<M, true, kSplitWaves, kSplitDepth>(x, ldx, w, ldw, y, ldy, y_type, N,
                                                              K, split_bytes, stream);
+  }
   return launch_mfma_cfg<M, false, kMfmaWaves, kMfmaDepth>(x, ldx, w, ldw, y, ldy, y_type, N, K,
                                                           xbytes, stream);
 }

@@ -982,6 +982,10 @@ __global__ __launch_bounds__(NW * kWave) void int4_gemv_mfma(
             };
             f32x4 sum = part_sum(lane);
             // a loop, so that one part's reads are in registers at a time
+            // (with two parts the compiler peels its one pass, which holds
+            // both parts' reads: 106 instead of 68 VGPRs, and measured
+            // faster than a loop it cannot peel, 1536 x 6912 at M = 8: 6.2
+            // against 6.5 us)
 #pragma unroll 1
             for (int hp = 1; hp < KS; ++hp) {
               const f32x4 ps = part_sum(lane + hp * (TR + 16 * (TR / 4)));
@@ -1196,18 +1200,6 @@ inline int mfma_chunk_items(int M, int K) {
   return C - (nph - 1) * cp >= NW ? cp : 0;
 }
 
-// k parts of the split matrix-core kernel: 1, or 2 (4) when 16-row (8-row)
-// tiles number fewer than the CUs, the parts divide the row's items, every
-// wave keeps at least one step, and M fits the A rows of a part.
-inline int mfma_k_parts(int M, int N, int K) {
-  const int C = K / 128, cus = device_cus();
-  int ks = 1;
-  while (ks < 4 && (N + 16 / ks - 1) / (16 / ks) < cus && M <= 8 / ks && C % (2 * ks) == 0 &&
-         C / (2 * ks) >= kSplitWaves)
-    ks *= 2;
-  return ks;
-}
-
 // Whole tiles per wave when the tiles fill at least half of the resident
 // wavefront slots; otherwise (and when every wave gets at least one item and
 // the partial sums fit in LDS) the waves of a workgroup split each tile.
@@ -1236,7 +1228,7 @@ hipError_t launch_mfma_ppb(const uint16_t* x, int64_t ldx, const uint8_t* w,
       // wavefronts per workgroup: 16 measured slower, 1536 x 6912 at M = 8
       // 7.9 against 6.2 us; so did k parts in the packed layout's kernel,
       // 7.0 against 6.8 us for its 16-row tiles over 16 wavefronts)
-      switch (mfma_k_parts(M, N, K)) {
+      switch (mfma_k_parts(M, N, K, kSplitWaves)) {
         case 4:
           if constexpr (M <= 4)
             return launch_mfma_cfg<M, PPB, true, false, 4>(x, ldx, w, scales, zp, y, ldy, y_type,

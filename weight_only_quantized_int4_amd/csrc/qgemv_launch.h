@@ -157,6 +157,20 @@ inline int device_cus() {
   return cached[dev];
 }
 
+// k parts of a split matrix-core kernel (16 x 16 MFMA tiles whose columns
+// may carry 16 / ks weight rows in ks parts of their k range): 1, or 2 (4)
+// while 16-row (8-row) tiles number fewer than the CUs, the parts divide the
+// row's 128-weight items, each of the `waves` wavefronts keeps at least one
+// step, and M fits the A rows of a part.
+inline int mfma_k_parts(int M, int N, int K, int waves) {
+  const int C = K / 128, cus = device_cus();
+  int ks = 1;
+  while (ks < 4 && (N + 16 / ks - 1) / (16 / ks) < cus && M <= 8 / ks && C % (2 * ks) == 0 &&
+         C / (2 * ks) >= waves)
+    ks *= 2;
+  return ks;
+}
+
 // Raise `kernel`'s dynamic-LDS limit to `bytes` when that is above 64 KB
 // (once per kernel, device and size).
 template <typename F>
