@@ -250,9 +250,11 @@ def test_random_shapes_offsets_and_strides(case):
 
 # k parts of the split matrix-core kernel: where 16-row tiles leave CUs idle,
 # the MFMA columns carry 8 rows in 2 parts of their k range (M <= 8) or 4
-# rows in 4 parts (M <= 4); one workgroup per tile of 16 / ks rows.
+# rows in 4 parts (M <= 4); one workgroup per tile of 16 / ks rows (rows of
+# 12 items: 4 wavefronts per workgroup).
 @pytest.mark.parametrize("N,K,M,ks", [(1536, 6912, 3, 2), (1003, 4096, 4, 4), (777, 2048, 6, 2),
-                                      (1001, 2048, 8, 2), (203, 4096, 2, 4), (250, 8192, 5, 2)])
+                                      (1001, 2048, 8, 2), (203, 4096, 2, 4), (250, 8192, 5, 2),
+                                      (1536, 1536, 3, 2), (256, 1536, 8, 2)])
 def test_matrix_core_k_parts(N, K, M, ks):
     p = bf16_case(N, K, 390 + M)
     say(f"bf16 k parts N={N} K={K} M={M} ks={ks}")
@@ -264,7 +266,8 @@ def test_matrix_core_k_parts(N, K, M, ks):
     assert_accept(y_host(y), yr, S, "f32", f"bf16 k parts {N}x{K} M={M}")
 
 
-@pytest.mark.parametrize("K,M,ks", [(4096, 4, 4), (4096, 3, 4), (2048, 8, 2), (8192, 5, 2)])
+@pytest.mark.parametrize("K,M,ks", [(4096, 4, 4), (4096, 3, 4), (2048, 8, 2), (8192, 5, 2),
+                                     (1536, 3, 2), (1536, 6, 2)])
 def test_one_hot_probe_k_parts_is_bit_exact(K, M, ks):
     """Row r of x one-hot at k_r (every 128-wide item and its seams probed, so
     every part of every step): y[r, n] must equal the oracle's y, which is

@@ -303,11 +303,12 @@ def test_wide_matrix_sampled(bs, asym, M):
 
 @pytest.mark.parametrize("N,K,bs,mfma", [(4096, 4096, 128, True), (4100, 11008, 32, True),
                                          (2064, 4096, 64, True), (4096, 4096, 32, False),
-                                         (1536, 6912, 128, False), (2048, 1536, 64, False)])
+                                         (1536, 6912, 128, True), (2048, 1536, 64, True),
+                                         (1536, 4096, 32, False)])
 def test_two_rows_kernel_choice(N, K, bs, mfma):
     """M = 2 runs on the matrix cores except with blocks of 32 along rows of at
-    most 4096 weights, or on matrices of at most 2048 rows (v_dot2); both
-    kernels meet the tolerance on every column."""
+    most 4096 weights (v_dot2); both kernels meet the tolerance on every
+    column."""
     say(f"int4 M=2 N={N} K={K} bs={bs} mfma={mfma}")
     p = int4_case(N, K, bs, True, 740 + bs)
     y = y_host(_run(p, 2, torch.float32))
@@ -472,14 +473,17 @@ def test_random_shapes_and_strides(case):
 
 # k parts of the split matrix-core kernel: where 16-row tiles leave CUs idle,
 # the MFMA columns carry 8 rows in 2 parts of their k range (M <= 8) or 4 rows
-# in 4 parts (M <= 4); the grid is one workgroup per tile of 16 / ks rows.
+# in 4 parts (M <= 4); the grid is one workgroup per tile of 16 / ks rows
+# (rows of 12 items: 4 wavefronts per workgroup).
 @pytest.mark.parametrize("N,K,bs,asym,M,ks", [(1000, 4096, 32, True, 3, 4),
                                               (1003, 4096, 64, True, 4, 4),
                                               (1003, 4096, 128, False, 4, 4),
                                               (777, 2048, 256, True, 6, 2),
                                               (250, 8192, 32, True, 5, 2),
                                               (1001, 2048, 64, True, 8, 2),
-                                              (1536, 6912, 128, False, 7, 2)])
+                                              (1536, 6912, 128, False, 7, 2),
+                                              (1536, 1536, 128, False, 5, 2),
+                                              (300, 1536, 32, True, 3, 2)])
 def test_matrix_core_k_parts(N, K, bs, asym, M, ks):
     say(f"int4 matrix-core k parts N={N} K={K} bs={bs} asym={asym} M={M} ks={ks}")
     p = int4_case(N, K, bs, asym, 1500 + M)
@@ -492,7 +496,7 @@ def test_matrix_core_k_parts(N, K, bs, asym, M, ks):
 
 @pytest.mark.parametrize("K,bs,M,ks", [(4096, 32, 4, 4), (4096, 64, 3, 4), (4096, 256, 4, 4),
                                        (2048, 32, 8, 2), (2048, 128, 5, 2), (8192, 64, 4, 4),
-                                       (8192, 32, 6, 2)])
+                                       (8192, 32, 6, 2), (1536, 64, 4, 2), (1536, 32, 7, 2)])
 def test_one_hot_probe_k_parts_is_bit_exact(K, bs, M, ks):
     """Row r of x is one-hot at k_r (positions across every item and at item
     seams, so every part of every step is probed); y[r, n] must equal the

@@ -529,8 +529,23 @@ hipError_t launch_mfma(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_
         return launch_mfma_cfg<M, true, kSplitWaves, kSplitDepth, 2>(x, ldx, w, ldw, y, ldy,
                                                                     y_type, N, K, split_bytes,
                                                                     stream);
-      default:
-        break;
+      default: {
+        // rows too short for 8 wavefronts a step each in parts (e.g. 12
+        // items): 4 wavefronts per workgroup
+        const size_t bytes4 = xbytes + (size_t)4 * kWave * 16;
+        switch (mfma_k_parts(M, N, K, 4)) {
+          case 4:
+            if constexpr (M <= 4)
+              return launch_mfma_cfg<M, true, 4, kSplitDepth, 4>(x, ldx, w, ldw, y, ldy, y_type,
+                                                                 N, K, bytes4, stream);
+            break;
+          case 2:
+            return launch_mfma_cfg<M, true, 4, kSplitDepth, 2>(x, ldx, w, ldw, y, ldy, y_type, N,
+                                                               K, bytes4, stream);
+          default:
+            break;
+        }
+      }
     }
     return launch_mfma_cfg<M, true, kSplitWaves, kSplitDepth>(x, ldx, w, ldw, y, ldy, y_type, N,
                                                              K, split_bytes, stream);

@@ -1158,12 +1158,12 @@ constexpr int kMfmaDepth = 1;
 constexpr int kSplitWaves = 8;
 constexpr int kSplitDepth = 1;
 
-template <int M, int PPB, bool SPLIT, bool PHASED = false, int KS = 1>
+template <int M, int PPB, bool SPLIT, bool PHASED = false, int KS = 1, int NWS = kSplitWaves>
 hipError_t launch_mfma_cfg(const uint16_t* x, int64_t ldx, const uint8_t* w,
                            const uint16_t* scales, const uint8_t* zp, void* y, int64_t ldy,
                            int y_type, int N, int K, int block_size, size_t shmem, int cp,
                            hipStream_t stream) {
-  constexpr int NW = SPLIT ? kSplitWaves : kMfmaWaves;
+  constexpr int NW = SPLIT ? NWS : kMfmaWaves;
   constexpr int DG = SPLIT ? kSplitDepth : kMfmaDepth;
   constexpr int TR = 16 / KS;
   const int bs_log2 = __builtin_ctz((unsigned)block_size);
@@ -1238,8 +1238,23 @@ hipError_t launch_mfma_ppb(const uint16_t* x, int64_t ldx, const uint8_t* w,
         case 2:
           return launch_mfma_cfg<M, PPB, true, false, 2>(x, ldx, w, scales, zp, y, ldy, y_type, N,
                                                          K, block_size, split_bytes, 0, stream);
-        default:
-          break;
+        default: {
+          // rows too short for 8 wavefronts a step each in parts (e.g. 12
+          // items): 4 wavefronts per workgroup
+          const size_t bytes4 = xbytes + (size_t)4 * kWave * 16;
+          switch (mfma_k_parts(M, N, K, 4)) {
+            case 4:
+              if constexpr (M <= 4)
+                return launch_mfma_cfg<M, PPB, true, false, 4, 4>(
+                    x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, bytes4, 0, stream);
+              break;
+            case 2:
+              return launch_mfma_cfg<M, PPB, true, false, 2, 4>(
+                  x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, bytes4, 0, stream);
+            default:
+              break;
+          }
+        }
       }
       return launch_mfma_cfg<M, PPB, true>(x, ldx, w, scales, zp, y, ldy, y_type, N, K,
                                            block_size, split_bytes, K / 128, stream);
@@ -1281,12 +1296,12 @@ hipError_t launch_m(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint
     // cores) with blocks of 32 along rows of at most 4096 weights, where the
     // matrix-core kernel's per-block scaling and lane swaps cost more than
     // v_dot2 spends on a second row (4096 x 4096 6.0 / 6.8, 14336 x 4096
-    // 11.7 / 12.4, 32000 x 4096 18.7 / 19.8, 11008 x 4096 10.1 / 10.4), and
-    // on matrices of at most 2048 rows, whose few 16-row tiles the
-    // matrix-core kernel spreads less well (1536 x 6912: blocks of 64 6.5 /
-    // 8.0, blocks of 128 6.4 / 7.1).  With longer rows, or blocks of 64 or
-    // more on taller matrices, the matrix cores win.
-    const bool dot2_pair = M == 2 && ((block_size == 32 && K <= 4096) || N <= 2048);
+    // 11.7 / 12.4, 32000 x 4096 18.7 / 19.8, 11008 x 4096 10.1 / 10.4).  With
+    // longer rows, or blocks of 64 or more, the matrix cores win, on short
+    // matrices through the k parts of the split kernel (1536 x 6912, blocks
+    // of 128: v_dot2 6.3, matrix cores in 16-row tiles 7.1, in parts 5.1;
+    // 1536 x 1536: 4.4 against 3.4).
+    const bool dot2_pair = M == 2 && block_size == 32 && K <= 4096;
     if (K % 128 == 0 && aligned && !dot2_pair &&
         ((size_t)M * K * 2 <= (size_t)kLdsMax || mfma_chunk_items(M, K) != 0))
       return launch_mfma<M>(x, ldx, w, scales, zp, y, ldy, y_type, N, K, block_size, stream);
