@@ -202,3 +202,48 @@ def test_failed_registration_is_dropped_with_the_weight(fake_abi, monkeypatch):
     del w
     gc.collect()
     assert key not in dispatch._failed
+
+
+def test_int4_packed_copy_choice_and_lifetime(fake_abi, monkeypatch):
+    """A registered packed copy serves row groups of >= 2 rows of x on
+    matrices of at least as many 16-row tiles as CUs; single rows, short
+    matrices and unregistered weights keep the original layout.  The entry
+    is dropped with the weight tensor."""
+    import gc
+
+    def repack(w, s, z, packed, bs, layout=1, stream=None):
+        fake_abi.append(("repack", w.shape[0], bs))
+        return packed
+
+    def packed_gemv(x, packed, y, bs, layout=1, stream=None):
+        fake_abi.append(("packed", x.shape[0], y.shape[0]))
+        return y
+
+    monkeypatch.setattr(qgemv, "int4_packed_bytes", lambda N, K, bs, layout=1: 0 if K % 128 else N * K)
+    monkeypatch.setattr(qgemv, "int4_repack", repack)
+    monkeypatch.setattr(qgemv, "qgemv_int4_packed", packed_gemv)
+    monkeypatch.setattr(dispatch, "_compute_units", lambda device: 4)
+    tall = torch.zeros((64, 128), dtype=torch.uint8)   # 4 tiles of 16 rows = the 4 CUs
+    short = torch.zeros((48, 128), dtype=torch.uint8)  # 3 tiles
+    s = torch.zeros((64, 8), dtype=torch.float16)
+    assert dispatch.register_int4_packed(tall, s, None, 32)
+    assert dispatch.register_int4_packed(short, s[:48], None, 32)
+    assert not dispatch.register_int4_packed(torch.zeros((64, 100), dtype=torch.uint8), s, None, 40)
+    assert fake_abi == [("repack", 64, 32), ("repack", 48, 32)]
+    del fake_abi[:]
+    x = torch.zeros((11, 256), dtype=torch.float16)
+    dispatch.int4_linear(x, tall, s, None, 32)          # groups of 8 and 3 rows
+    dispatch.int4_linear(x[:1], tall, s, None, 32)      # one row: original layout
+    dispatch.int4_linear(x[:9], tall, s, None, 32)      # 8 + 1
+    dispatch.int4_linear(x[:3], short, s[:48], None, 32)  # short matrix
+    dispatch.int4_linear(x[:3], tall, s, None, 64)      # no copy for this block size
+    assert fake_abi == [("packed", 8, 8), ("packed", 3, 3), ("int4", 1, 1), ("packed", 8, 8),
+                        ("int4", 1, 1), ("int4", 3, 3), ("int4", 3, 3)]
+    assert dispatch.int4_liveness() == {dispatch.LABEL_INT4: 4, dispatch.LABEL_INT4_PACKED: 3}
+    key = dispatch._int4_key(tall, 32)
+    assert dispatch.int4_packed_of(tall, 32) is not None
+    dispatch.unregister_int4_packed(short, 32)
+    assert dispatch.int4_packed_of(short, 32) is None
+    del tall
+    gc.collect()
+    assert key not in dispatch._packed

@@ -156,3 +156,42 @@ def test_prefill_arm_is_the_prefill_product():
     yg, Sg = oracle.q4k_gemv(datagen.prefill_x(T, K, 436), p.w, T, N, K)
     assert_accept(y_host(y_rows), yg, Sg, "f32", "dispatch q4k rows T=40")
     dispatch.unregister_q4k_plane(wd)
+
+
+def test_int4_packed_copy_serves_tall_matrices():
+    """A registered packed copy of a matrix of more 16-row tiles than CUs
+    serves the row groups of >= 2 rows (8 + 3 here) and the single row stays on
+    the original layout; all within the bound of the oracle.  A short matrix
+    keeps the original layout although its copy is registered."""
+    N, K, bs = 4100, 1024, 64
+    say("dispatch int4 packed copy")
+    p = int4_case(N, K, bs, True, 433)
+    wd, sd, zd = to_dev(p.w), f16_dev(p.scales), to_dev(p.zp)
+    assert dispatch.register_int4_packed(wd, sd, zd, bs)
+    assert dispatch.int4_packed_of(wd, bs) is not None
+    dispatch.reset_liveness()
+    M = 11
+    xr = np.concatenate([p.x, p.x ^ np.uint16(0x8000)])[:M]
+    y = dispatch.int4_linear(f16_dev(xr), wd, sd, zd, bs,
+                             torch.empty((M, N), dtype=torch.float32, device=DEV))
+    assert dispatch.explain().startswith("int4_packed M=3"), dispatch.explain()
+    y1 = dispatch.int4_linear(f16_dev(p.x[:1]), wd, sd, zd, bs,
+                              torch.empty((1, N), dtype=torch.float32, device=DEV))
+    assert dispatch.explain().startswith("int4_span M=1") or \
+        dispatch.explain().startswith("int4_dot2"), dispatch.explain()
+    assert dispatch.int4_liveness() == {dispatch.LABEL_INT4: 1, dispatch.LABEL_INT4_PACKED: 2}
+    yr, S = int4_ref(N, K, bs, True, 433)
+    yref = np.concatenate([yr, -yr])[:M]
+    Sref = np.concatenate([S, S])[:M]
+    assert_accept(y_host(y), yref, Sref, "f32", "int4 packed copy M=11")
+    assert_accept(y_host(y1), yr[:1], S[:1], "f32", "int4 packed copy M=1")
+    # short matrix: the original layout's k-part kernel
+    ps = int4_case(1536, 1536, 128, False, 201)
+    ws, ss = to_dev(ps.w), f16_dev(ps.scales)
+    assert dispatch.register_int4_packed(ws, ss, None, 128)
+    dispatch.int4_linear(f16_dev(ps.x[:4]), ws, ss, None, 128,
+                         torch.empty((4, 1536), dtype=torch.float32, device=DEV))
+    assert dispatch.explain().startswith("int4_mfma_split M=4"), dispatch.explain()
+    dispatch.unregister_int4_packed(wd, bs)
+    dispatch.unregister_int4_packed(ws, 128)
+    assert dispatch.int4_packed_of(wd, bs) is None

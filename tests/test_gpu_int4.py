@@ -523,3 +523,21 @@ def test_one_hot_probe_k_parts_is_bit_exact(K, bs, M, ks):
         assert np.array_equal(got, want), kk
         nz = want != 0
         assert np.array_equal(got.view(np.uint32)[nz], want.view(np.uint32)[nz]), kk
+
+
+def test_k_parts_strided_unaligned_x_and_strided_y():
+    """The k-part split kernel (4 parts: 1003 rows, M = 4) with x rows at a
+    2-byte offset and ldx = K + 3 (x staged element-wise) and y rows of
+    stride N + 5."""
+    N, K, bs, M = 1003, 4096, 64, 4
+    say("int4 k parts, unaligned strided x, strided y")
+    p = int4_case(N, K, bs, True, 1590)
+    yr, S = int4_ref(N, K, bs, True, 1590)
+    buf = np.zeros(1 + M * (K + 3), dtype=np.uint16)
+    for m in range(M):
+        buf[1 + m * (K + 3):1 + m * (K + 3) + K] = p.x[m]
+    xt = f16_dev(buf)[1:].view(M, K + 3)[:, :K]
+    assert xt.data_ptr() % 16 == 2
+    y = y_host(_run(p, M, torch.float32, x=xt, ldy=N + 5))
+    assert f"int4_mfma_split M={M} grid={(N + 3) // 4} " in q.last_launch(), q.last_launch()
+    assert_accept(y, yr[:M], S[:M], "f32", "int4 k parts strided")
